@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule on one MI355X.
+
+Two legs, both on seeded synthetic inputs already resident in HBM:
+
+  decode   gdr_decode_step on the batched channelwise workload: B=64,
+           H_qk=16 -> H_v=32, dk=dv=128, bf16 packed q|k|v rows, fp32 state
+           (128 MiB), fresh inputs every step, the state carried from step to
+           step.  One bench step = one decode token for the whole batch.
+           Reported as state-update GB/s: the algorithmic bytes of a step
+           (state read + write, qkv, gate, beta, o) over its time.
+  prefill  gdr_prefill_chunked on B=1, T=4000, chunk 64, H 16 -> 32,
+           dk=dv=128, bf16, channelwise gate, zero initial state.  Reported as
+           tokens/s, with the fraction of the HBM and bf16 MFMA peaks.
+
+Prints one JSON line.  `value` is the decode GB/s; the prefill figures sit
+under "prefill".  Each leg carries its roofline (kernel time from HIP events
+recorded around every launch on the launch stream) and the fp64 CPU oracle
+timed on a bounded sample of the same workload ("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+import torch
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import gated_delta_rule_40_amd as gdr  # noqa: E402
+from gated_delta_rule_40_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode state-update GB/s (% of HBM peak); chunked prefill tokens/s"
+DEV = "cuda:0"
+
+
+def up(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
+
+
+def cpu_threads() -> int:
+    # The GPU machine gives one GPU a 16-core share, whatever os.cpu_count() says.
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        h.update((ROOT / "gated_delta_rule_40_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key: str, digest: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    on the current kernel source (else None)."""
+    p = ROOT / "profiles" / "hbm_traffic.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text()).get(kernel_key)
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def decode_bytes_per_step(B, H_qk, H_v, dk, dv) -> int:
+    state = 2 * B * H_v * dk * dv * 4
+    qkv = B * (2 * H_qk * dk + H_v * dv) * 2
+    gate = B * H_v * dk * 4
+    beta = B * H_v * 4
+    o = B * H_v * dv * 2
+    return state + qkv + gate + beta + o
+
+
+def bench_decode(K, W, B):
+    case = synth.batched_decode(seed=3, steps=256, B=B)
+    t = case.tensors
+    H_qk, H_v, dk, dv = case.H_qk, case.H_v, case.dk, case.dv
+    n_in = t["qkv"].shape[0]
+    qkv = up(t["qkv"])
+    g = up(t["gate_in"])
+    bl = up(t["beta_logit"])
+    S0 = up(t["S0"])
+    S = S0.clone()
+    o = torch.empty((B, H_v, dv), dtype=torch.bfloat16, device=DEV)
+    kw = dict(H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, gate=case.gate)
+
+    def step(i):
+        j = i % n_in
+        gdr.gdr_decode_step(qkv[j], g[j], bl[j], S, o, **kw)
+
+    for i in range(W):
+        step(i)
+    S.copy_(S0)  # pristine state, outside the timed region
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    region_ms = starts[0].elapsed_time(ends[-1])
+    nbytes = decode_bytes_per_step(B, H_qk, H_v, dk, dv)
+    kern_s = float(np.mean(per_launch_ms)) / 1e3
+    achieved = nbytes / kern_s / 1e9
+    digest = source_digest("decode.hip")
+    traffic = traffic_from_profile(f"decode_b{B}", digest)
+    return dict(
+        value=nbytes * K / wall / 1e9,
+        wall_s=wall,
+        ms_per_step=wall / K * 1e3,
+        region_event_ms=region_ms,
+        kernel_us_mean=kern_s * 1e6,
+        kernel_us_median=float(np.median(per_launch_ms)) * 1e3,
+        bytes_per_step=nbytes,
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic,
+                      kernel="gdr::decode_kernel<bf16,128,128>", source_digest=digest),
+        case=case,
+    )
+
+
+def cpu_decode(case, seconds):
+    import oracle
+
+    t = case.tensors
+    thr = oracle.threads_used(cpu_threads())
+    S = t["S0"].astype(np.float64)
+    steps = 0
+    t0 = time.perf_counter()
+    while steps < t["qkv"].shape[0]:
+        oracle.decode(synth.bf16_to_f32(t["qkv"][steps]), case.H_qk, case.H_v, case.dk, case.dv,
+                      case.gate, t["gate_in"][steps], t["beta_logit"][steps], S, threads=thr)
+        steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    nbytes = decode_bytes_per_step(case.B, case.H_qk, case.H_v, case.dk, case.dv)
+    return dict(value=nbytes * steps / el / 1e9, unit="GB/s", cores=thr, kind="oracle",
+                sample=f"{steps} consecutive decode steps of the B={case.B} batch "
+                       f"({el:.1f} s, fp64 C recurrence, OpenMP over (b,h))")
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def prefill_flops(T, B, H_v, dk, dv, C) -> float:
+    per = 6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3
+    return per * T * B * H_v
+
+
+def prefill_bytes(T, B, H_qk, H_v, dk, dv, channel=True, state_in=False) -> int:
+    per_tok = 2 * H_qk * dk * 2 + H_v * dv * 2 + (H_v * dk if channel else H_v) * 4 \
+        + H_v * 4 + H_v * dv * 2
+    state = B * H_v * dk * dv * 4 * (2 if state_in else 1)
+    return per_tok * T * B + state
+
+
+def bench_prefill(reps, warm):
+    case = synth.prefill(seed=4)
+    t = case.tensors
+    B, T, C = case.B, case.T, case.chunk
+    H_qk, H_v, dk, dv = case.H_qk, case.H_v, case.dk, case.dv
+    q, k, v = up(t["q"]), up(t["k"]), up(t["v"])
+    g, bl = up(t["gate_in"]), up(t["beta_logit"])
+    S = torch.empty((B, H_v, dk, dv), dtype=torch.float32, device=DEV)
+    o = torch.empty((B, T, H_v, dv), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(gdr.gdr_prefill_workspace_size(B, T, H_qk, H_v, dk, dv, C, torch.bfloat16,
+                                                    case.gate), dtype=torch.uint8, device=DEV)
+    kw = dict(H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, chunk=C, gate=case.gate)
+
+    def run():
+        gdr.gdr_prefill_chunked(q, k, v, g, bl, None, S, o, ws, **kw)
+
+    for _ in range(warm):
+        run()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        starts[i].record()
+        run()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    sec = float(np.mean(ms)) / 1e3
+    flops = prefill_flops(T, B, H_v, dk, dv, C)
+    nbytes = prefill_bytes(T, B, H_qk, H_v, dk, dv, channel=True, state_in=False)
+    return dict(
+        value=B * T / sec,
+        unit="tokens/s",
+        ms_per_call=sec * 1e3,
+        wall_tokens_per_s=B * T * reps / wall,
+        workload=f"prefill_t{T}: B={B}, T={T} (62 chunks of 64 + 32), H_qk={H_qk}->H_v={H_v}, "
+                 f"dk=dv={dk}, chunk {C}, channelwise gate, bf16 io, zero initial state",
+        dtype="bf16",
+        roofline=dict(bound="hbm", achieved=nbytes / sec / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                      mfma_achieved_tflops=flops / sec / 1e12,
+                      mfma_peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+                      mfma_frac=flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      algorithmic_bytes=nbytes, algorithmic_flops=flops,
+                      traffic=traffic_from_profile("prefill_t4000",
+                                                   source_digest("prefill.hip"))),
+        case=case,
+    )
+
+
+def cpu_prefill(case, seconds):
+    import oracle
+
+    t = case.tensors
+    thr = oracle.threads_used(cpu_threads())
+    # Whole sequences of value heads (b=0), `thr` heads at a time, until time is up.
+    rep = case.H_v // case.H_qk
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < case.H_v:
+        hs = list(range(heads, min(case.H_v, heads + thr)))
+        hq = sorted({h // rep for h in hs})
+        # heads in hs use query/key heads hq; pass a sub-problem with those heads
+        sub_q = synth.bf16_to_f32(t["q"][:, :, hq[0]:hq[-1] + 1])
+        sub_k = synth.bf16_to_f32(t["k"][:, :, hq[0]:hq[-1] + 1])
+        lo = hq[0] * rep
+        hi = (hq[-1] + 1) * rep
+        oracle.sequence(sub_q, sub_k, synth.bf16_to_f32(t["v"][:, :, lo:hi]), case.gate,
+                        t["gate_in"][:, :, lo:hi], t["beta_logit"][:, :, lo:hi],
+                        t["S0"][:, lo:hi], threads=thr)
+        heads = hi
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    frac = heads / case.H_v
+    return dict(value=case.B * case.T * frac / el, unit="tokens/s", cores=thr, kind="oracle",
+                sample=f"{heads} of {case.H_v} value heads over all {case.T} tokens "
+                       f"({el:.1f} s, fp64 token recurrence, OpenMP over heads); "
+                       f"tokens/s scaled to all heads")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed decode steps")
+    ap.add_argument("--batch", type=int, default=64, help="decode batch (64 is the workload)")
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--legs", default="decode,prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time box of each CPU-oracle baseline (0 disables)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the (batch, head) units shard across GPUs without communication, so one GPU's "
+              f"figure is the per-GPU figure)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gdr.load_library()
+    legs = set(args.legs.split(","))
+    out = {"metric": METRIC}
+
+    dec = None
+    if "decode" in legs:
+        dec = bench_decode(args.steps, args.warmup, args.batch)
+        print(f"[bench] decode done: {dec['value']:.1f} GB/s", file=sys.stderr, flush=True)
+    pre = None
+    if "prefill" in legs:
+        pre = bench_prefill(args.prefill_reps, args.prefill_warmup)
+        print(f"[bench] prefill done: {pre['value']:.3e} tok/s", file=sys.stderr, flush=True)
+
+    cpu_dec = cpu_pre = None
+    if args.cpu_seconds > 0:
+        if dec is not None:
+            cpu_dec = cpu_decode(dec["case"], args.cpu_seconds)
+        if pre is not None:
+            cpu_pre = cpu_prefill(pre["case"], args.cpu_seconds)
+        print("[bench] cpu baselines done", file=sys.stderr, flush=True)
+
+    if dec is not None:
+        out.update({
+            "value": dec["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"batched_decode_b{args.batch}: B={args.batch}, H_qk=16->H_v=32, "
+                                   f"dk=dv=128, channelwise gate, bf16 packed q|k|v, fp32 state, "
+                                   f"fresh inputs per step",
+                       "batch": args.batch, "bytes_per_step": dec["bytes_per_step"],
+                       "hbm_peak_frac_of_wall": dec["value"] / HBM_PEAK_GBS},
+            "kernel_us_mean": dec["kernel_us_mean"], "kernel_us_median": dec["kernel_us_median"],
+            "roofline": dec["roofline"],
+            "cpu_baseline": cpu_dec,
+        })
+    if pre is not None:
+        p = {k: v for k, v in pre.items() if k != "case"}
+        p["cpu_baseline"] = cpu_pre
+        out["prefill"] = p
+        if dec is None:
+            out.update({"value": pre["value"], "unit": "tokens/s", "n_gpus": 1,
+                        "steps": args.prefill_reps, "warmup": args.prefill_warmup,
+                        "ms_per_step": pre["ms_per_call"], "higher_is_better": True,
+                        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                        "data": "synthetic", "config": {"workload": pre["workload"]},
+                        "roofline": pre["roofline"], "cpu_baseline": cpu_pre})
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,84 @@
+// device_common.hpp -- small gfx950 device helpers: bf16 <-> fp32, vector
+// loads/stores of io-dtype rows, wave64 reductions and the gate functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+using bf16 = __bf16;
+
+constexpr float kL2Eps = 1e-6f;  // x / sqrt(sum x^2 + eps)
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Load N contiguous io-dtype values (16-byte aligned when N*sizeof(T) >= 16)
+// and widen them to fp32.
+template <typename T, int N>
+__device__ __forceinline__ void load_row(const T* __restrict__ p, float (&out)[N]) {
+  constexpr int kBytes = N * static_cast<int>(sizeof(T));
+  if constexpr (kBytes % 16 == 0) {
+    constexpr int kPer = 16 / static_cast<int>(sizeof(T));
+#pragma unroll
+    for (int c = 0; c < N / kPer; ++c) {
+      uint4 raw = reinterpret_cast<const uint4*>(p)[c];
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) out[c * kPer + u] = to_f32(e[u]);
+    }
+  } else if constexpr (kBytes % 8 == 0) {
+    constexpr int kPer = 8 / static_cast<int>(sizeof(T));
+#pragma unroll
+    for (int c = 0; c < N / kPer; ++c) {
+      uint2 raw = reinterpret_cast<const uint2*>(p)[c];
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) out[c * kPer + u] = to_f32(e[u]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < N; ++u) out[u] = to_f32(p[u]);
+  }
+}
+
+// Store 4 fp32 values as io dtype (8 or 16 bytes, aligned).
+template <typename T>
+__device__ __forceinline__ void store4(T* __restrict__ p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  } else {
+    T e[4] = {from_f32<T>(a), from_f32<T>(b), from_f32<T>(c), from_f32<T>(d)};
+    *reinterpret_cast<uint2*>(p) = *reinterpret_cast<const uint2*>(e);
+  }
+}
+
+// Sum over the 64 lanes of a wave; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// softplus(z) = log(1 + e^z), written so that large |z| neither overflows nor
+// loses the linear tail.
+__device__ __forceinline__ float softplusf(float z) {
+  return z > 0.0f ? z + log1pf(expf(-z)) : log1pf(expf(z));
+}
+
+// Fused GatedDeltaNet scalar log-decay: -exp(A_log) * softplus(x + dt_bias).
+__device__ __forceinline__ float fused_log_decay(float x, float A_log, float dt_bias) {
+  return -expf(A_log) * softplusf(x + dt_bias);
+}
+
+}  // namespace gdr

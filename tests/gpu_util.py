@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU tests: device upload of seeded inputs, the
+relative-error measure and the tolerances.
+
+Tolerance (relative to the fp64 oracle, per tensor, separately for o and the
+final state): err = max|x - ref| / max|ref| must stay below 1e-4 when q/k/v
+are fp32 and below 2e-2 when they are bf16.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_40_amd as gdr
+from gated_delta_rule_40_amd import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdr.load_library()  # raises if libgdr.so is missing: no fallback
+
+
+def announce(msg: str):
+    print(f"\n[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rel(x, ref) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(x - ref)))
+    return num / den if den > 0 else num
+
+
+def to_dev(a, io=None):
+    """numpy -> device tensor.  uint16 arrays are bf16 bit patterns."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def to_host(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def oracle_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def io_dtype(io: str):
+    return torch.bfloat16 if io == "bf16" else torch.float32
+
+
+def new_workspace(B, T, H_qk, H_v, dk, dv, chunk, io, gate):
+    n = gdr.gdr_prefill_workspace_size(B, T, H_qk, H_v, dk, dv, chunk, io_dtype(io), gate)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
+
+
+def run_prefill(case: synth.Case, chunk=None, state_in="S0", scale=1.0, l2norm=True,
+                T_slice=None, inplace=False, on_device=False):
+    """Run gdr_prefill_chunked on a seeded case; returns (o, state) on the host
+    as float64, or as device tensors with on_device=True."""
+    t = case.tensors
+    sl = slice(None) if T_slice is None else T_slice
+    q = to_dev(t["q"][:, sl])
+    k = to_dev(t["k"][:, sl])
+    v = to_dev(t["v"][:, sl])
+    g = to_dev(t["gate_in"][:, sl])
+    bl = to_dev(t["beta_logit"][:, sl])
+    B, T = q.shape[0], q.shape[1]
+    C = chunk or case.chunk
+    if isinstance(state_in, str):
+        s_in = to_dev(t[state_in])
+    else:
+        s_in = None if state_in is None else to_dev(np.asarray(state_in, np.float32))
+    s_out = s_in if (inplace and s_in is not None) else torch.empty(
+        (B, case.H_v, case.dk, case.dv), dtype=torch.float32, device=DEV)
+    o = torch.empty((B, T, case.H_v, case.dv), dtype=io_dtype(case.io), device=DEV)
+    ws = new_workspace(B, T, case.H_qk, case.H_v, case.dk, case.dv, C, case.io, case.gate)
+    gdr.gdr_prefill_chunked(q, k, v, g, bl, s_in, s_out, o, ws, H_qk=case.H_qk, H_v=case.H_v,
+                            dk=case.dk, dv=case.dv, chunk=C, gate=case.gate,
+                            A_log=to_dev(t["A_log"]), dt_bias=to_dev(t["dt_bias"]), scale=scale,
+                            l2norm_qk=l2norm)
+    torch.cuda.synchronize()
+    if on_device:
+        return o, s_out
+    return to_host(o), to_host(s_out)

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status before
+anything is launched."""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import gated_delta_rule_40_amd as gdr
+from gated_delta_rule_40_amd.binding import gdr_dims
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "gdr.h"
+E = dict(OK=0, NULL=-1, SHAPE=-2, DTYPE=-3, UNSUPPORTED=-4, WORKSPACE=-5, HIP=-6, ALIAS=-7,
+         ALIGN=-8)
+A = 0x10000  # fake, 16-byte aligned device addresses: never dereferenced here
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gdr_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(gdr.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(gdr.binding.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_status_values_match():
+    text = HEADER.read_text()
+    for k, v in E.items():
+        assert re.search(rf"GDR_(E_)?{k}\s*=\s*{v}\b", text), k
+
+
+def test_strerror_covers_every_status():
+    msgs = {v: gdr.gdr_strerror(v) for v in E.values()}
+    assert len(set(msgs.values())) == len(msgs)
+    assert gdr.gdr_strerror(-99) == "unknown gdr status"
+
+
+def _dims(B=2, T=5, H_qk=2, H_v=4, dk=32, dv=64, chunk=16):
+    return gdr_dims(B, T, H_qk, H_v, dk, dv, chunk)
+
+
+def decode(dims, io=0, gate=0, qkv=A, g=A + 0x100000, Al=None, dt=None, bl=A + 0x200000,
+           st=A + 0x300000, o=A + 0x4000000):
+    lib = gdr.load_library()
+    return lib.gdr_decode_step(ctypes.byref(dims) if dims is not None else None, io, gate, qkv,
+                               g, Al, dt, bl, st, o, 1.0, 1, None)
+
+
+def prefill(dims, io=0, gate=0, q=A, k=A + 0x1000000, v=A + 0x2000000, g=A + 0x3000000, Al=None,
+            dt=None, bl=A + 0x4000000, s_in=A + 0x5000000, s_out=A + 0x6000000, o=A + 0x7000000,
+            ws=A + 0x10000000, ws_bytes=None):
+    lib = gdr.load_library()
+    if ws_bytes is None:
+        ws_bytes = lib.gdr_prefill_workspace_size(ctypes.byref(dims), io, gate)
+    return lib.gdr_prefill_chunked(ctypes.byref(dims) if dims is not None else None, io, gate,
+                                   q, k, v, g, Al, dt, bl, s_in, s_out, o, 1.0, 1, ws, ws_bytes,
+                                   None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=None), "NULL"),
+    (dict(io=2), "DTYPE"),
+    (dict(gate=3), "DTYPE"),
+    (dict(dims=_dims(H_qk=3, H_v=4)), "SHAPE"),
+    (dict(dims=_dims(B=-1)), "SHAPE"),
+    (dict(dims=_dims(dk=48)), "UNSUPPORTED"),
+    (dict(dims=_dims(dv=256)), "UNSUPPORTED"),
+    (dict(qkv=None), "NULL"),
+    (dict(st=None), "NULL"),
+    (dict(g=None), "NULL"),
+    (dict(gate=2), "NULL"),                      # fused gate without A_log / dt_bias
+    (dict(qkv=A + 8), "ALIGN"),
+    (dict(st=A + 0x300004), "ALIGN"),
+    (dict(o=A + 0x300000), "ALIAS"),              # o on top of the state
+    (dict(o=A), "ALIAS"),                         # o on top of qkv
+    (dict(dims=_dims(B=0)), "OK"),                # nothing to do, nothing launched
+])
+def test_decode_validation(case, expect):
+    kw = dict(case)
+    dims = kw.pop("dims", _dims())
+    assert decode(dims, **kw) == E[expect]
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=_dims(T=-1)), "SHAPE"),
+    (dict(dims=_dims(chunk=8)), "UNSUPPORTED"),
+    (dict(dims=_dims(chunk=128)), "UNSUPPORTED"),
+    (dict(dims=_dims(dk=8)), "UNSUPPORTED"),
+    (dict(q=None), "NULL"),
+    (dict(s_out=None), "NULL"),
+    (dict(ws=None), "WORKSPACE"),
+    (dict(ws_bytes=16), "WORKSPACE"),
+    (dict(v=A + 0x2000004), "ALIGN"),
+    (dict(o=A + 0x2000000), "ALIAS"),              # o on top of v
+    (dict(o=A + 0x10000000), "ALIAS"),             # o on top of the workspace
+    (dict(dims=_dims(B=0)), "OK"),
+    (dict(dims=_dims(T=0), s_in=A + 0x6000000), "OK"),   # T=0, in place: nothing to copy
+])
+def test_prefill_validation(case, expect):
+    kw = dict(case)
+    dims = kw.pop("dims", _dims())
+    assert prefill(dims, **kw) == E[expect]
+
+
+def test_workspace_size_query():
+    lib = gdr.load_library()
+    size = lambda **kw: lib.gdr_prefill_workspace_size(ctypes.byref(_dims(**kw)), 1, 0)
+    assert size(T=0) == 0 and size(B=0) == 0
+    assert size(dk=48) == 0 and size(chunk=8) == 0
+    assert size(T=16) == size(T=1) > 0            # one chunk either way
+    assert size(T=17) == 2 * size(T=16)
+    assert size(B=4) == 2 * size(B=2)
+    assert size(T=64, chunk=64) == lib.gdr_prefill_workspace_size(ctypes.byref(_dims(T=64, chunk=64)), 1, 2)
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(RuntimeError):
+        gdr.load_library(tmp_path / "libgdr.so")

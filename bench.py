@@ -258,6 +258,17 @@ def cpu_prefill(case, seconds):
                        f"tokens/s scaled to all heads")
 
 
+def copy_calibration(reps=8, nbytes=256 << 20):
+    """A plain device copy of known size: what HBM byte counters read for it
+    calibrates them (FETCH_SIZE ~ nbytes, WRITE_SIZE ~ nbytes per dispatch)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=DEV)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return nbytes
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +301,10 @@ def main():
     if "prefill" in legs:
         pre = bench_prefill(args.prefill_reps, args.prefill_warmup)
         print(f"[bench] prefill done: {pre['value']:.3e} tok/s", file=sys.stderr, flush=True)
+
+    if "copy" in legs:
+        n = copy_calibration()
+        print(f"[bench] copy calibration done: {n} bytes per copy", file=sys.stderr, flush=True)
 
     cpu_dec = cpu_pre = None
     if args.cpu_seconds > 0:

@@ -5,7 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
-#include "../../include/gdr.h"
+#include "gdr.h"
 #include "gdr_internal.h"
 
 namespace {

@@ -23,7 +23,7 @@
 // across the row groups inside a wave (lane xor), then across waves in LDS.
 #include "device_common.hpp"
 #include "gdr_internal.h"
-#include "../../include/gdr.h"
+#include "gdr.h"
 
 namespace gdr {
 namespace {

@@ -32,7 +32,7 @@
 // fp32 MFMA for fp32 io); the triangular solve runs in fp32 in LDS.
 #include "device_common.hpp"
 #include "gdr_internal.h"
-#include "../../include/gdr.h"
+#include "gdr.h"
 
 namespace gdr {
 namespace {

@@ -1,0 +1,65 @@
+"""Decode steps and a chunked prefill captured in a HIP graph: every replay
+must reproduce the eager result exactly (same kernels, same inputs).  The
+replays are separated by eager work and synchronisation."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import gated_delta_rule_40_amd as gdr
+from gated_delta_rule_40_amd import synth
+from tests.gpu_util import DEV, announce, new_workspace, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager():
+    require_gpu()
+    announce("graph capture: 6 decode steps (B=4) + one prefill (T=100), 3 replays")
+    dec = synth.decode_case("graph", 71, 4, 6, 2, 4, 64, 64, "bf16", synth.GATE_CHANNEL,
+                            0.01, 0.5, 0.3)
+    td = dec.tensors
+    qkv, g, bl = to_dev(td["qkv"]), to_dev(td["gate_in"]), to_dev(td["beta_logit"])
+    S0 = to_dev(td["S0"])
+    S = S0.clone()
+    o = torch.empty((4, 4, 64), dtype=torch.bfloat16, device=DEV)
+    kw = dict(H_qk=2, H_v=4, dk=64, dv=64, gate=synth.GATE_CHANNEL)
+
+    pre = synth.prefill_case("graph_p", 72, 2, 100, 2, 4, 64, 64, 32, "bf16", synth.GATE_SCALAR,
+                             0.01, 0.3, 0.3)
+    tp = pre.tensors
+    pq, pk, pv = to_dev(tp["q"]), to_dev(tp["k"]), to_dev(tp["v"])
+    pg, pb, ps0 = to_dev(tp["gate_in"]), to_dev(tp["beta_logit"]), to_dev(tp["S0"])
+    ps = torch.empty_like(ps0)
+    po = torch.empty((2, 100, 4, 64), dtype=torch.bfloat16, device=DEV)
+    ws = new_workspace(2, 100, 2, 4, 64, 64, 32, "bf16", synth.GATE_SCALAR)
+    pkw = dict(H_qk=2, H_v=4, dk=64, dv=64, chunk=32, gate=synth.GATE_SCALAR)
+
+    def work():
+        for i in range(6):
+            gdr.gdr_decode_step(qkv[i], g[i], bl[i], S, o, **kw)
+        gdr.gdr_prefill_chunked(pq, pk, pv, pg, pb, ps0, ps, po, ws, **pkw)
+
+    work()
+    torch.cuda.synchronize()
+    ref = (S.clone(), o.clone(), ps.clone(), po.clone())
+
+    graph = torch.cuda.CUDAGraph()
+    S.copy_(S0)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            work()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        S.copy_(S0)            # eager work between replays
+        ps.zero_()
+        po.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (S, o, ps, po)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"

@@ -101,6 +101,56 @@ __device__ __forceinline__ void store_tile_t(OpT* Y, int ldy, int y_row0, int y_
   }
 }
 
+// Rows of the workspace block's operand regions are stored XOR-swizzled in
+// 16-byte pieces: piece p of row r sits at position p ^ swz_key(r, ppr), ppr
+// being the row's piece count.  For any 16 consecutive rows and a fixed p the
+// stored pieces then fall in 16 distinct groups of 4 LDS banks, so the MFMA
+// operand reads (16 rows, one piece each) are conflict-free after a straight
+// copy of the block into LDS.
+__host__ __device__ constexpr int swz_key(int r, int ppr) {
+  return ppr >= 16 ? (r & 15) : ((r / (16 / ppr)) % ppr);
+}
+
+// acc += X Z^T like mma_xzt, with X read from a swizzled block region whose
+// rows are `ppr` pieces wide; Z is a padded row-major LDS buffer.
+template <typename OpT, int KD>
+__device__ __forceinline__ f32x4 mma_swz(const OpT* __restrict__ X, int ppr, int x0,
+                                         const OpT* __restrict__ Z, int ldz, int z0, f32x4 acc,
+                                         int lane) {
+  constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));
+  const int r = lane & 15;
+  const int kg = lane >> 4;
+  const int key = swz_key(x0 + r, ppr);
+  const OpT* xrow = X + (x0 + r) * ppr * VPER;
+  auto xat = [&](int e) __attribute__((always_inline)) {
+    return xrow + (((e / VPER) ^ key) * VPER) + e % VPER;
+  };
+  if constexpr (sizeof(OpT) == 4) {
+#pragma unroll
+    for (int k = 0; k < KD; k += 4) {
+      float xa = *xat(k + kg);
+      float zb = Z[(z0 + r) * ldz + k + kg];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, zb, acc, 0, 0, 0);
+    }
+  } else if constexpr (KD % 32 == 0) {
+#pragma unroll
+    for (int k = 0; k < KD; k += 32) {
+      bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(xat(k + 8 * kg));
+      bf16x8_t zb = *reinterpret_cast<const bf16x8_t*>(Z + (z0 + r) * ldz + k + 8 * kg);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, zb, acc, 0, 0, 0);
+    }
+  } else {
+    static_assert(KD % 16 == 0, "contraction must be a multiple of 16");
+#pragma unroll
+    for (int k = 0; k < KD; k += 16) {
+      bf16x4_t xa = *reinterpret_cast<const bf16x4_t*>(xat(k + 4 * kg));
+      bf16x4_t zb = *reinterpret_cast<const bf16x4_t*>(Z + (z0 + r) * ldz + k + 4 * kg);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xa, zb, acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
 // Layout of one (b, h, chunk) block of the workspace.
 template <typename OpT, int DK, int C>
 struct ChunkBlock {
@@ -116,39 +166,69 @@ struct ChunkBlock {
 
 // ---------------------------------------------------------------------------
 // chunk_prep
+//
+// Per (b, h, chunk):
+//   1. every global load of the chunk is issued up front (rows of q and k for
+//      the L2 norms; per-thread channel columns of k, q, g for the decays);
+//   2. row norms, beta and the scalar gate per row;
+//   3. per-channel prefix sums (each channel split into row parts, combined
+//      through LDS) and the decayed operands, built in fp32 and rounded once;
+//   4. A and P on MFMA;
+//   5. (I + A)^-1 blocked by 16: the diagonal 16x16 blocks by forward
+//      substitution in registers (one lane per column), then the off-diagonal
+//      blocks level by level, T_ij = -T_ii sum_k A_ik T_kj, with fp32 MFMA;
+//   6. everything leaves through LDS in 16-byte coalesced stores.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <typename OpT, int DK, int C>
 struct PrepSmem {
-  static constexpr int LDK = DK + pad_of<OpT>();
-  static constexpr int LDA = C + 1;  // fp32 [C][C+1] for the solve
-  static constexpr int LDP = C + pad_of<OpT>();
+  static constexpr int LDK = DK + pad_of<OpT>();  // rows of Kt, Kh, Qt
+  static constexpr int LDC = C + pad_of<OpT>();   // rows of Ke^T and P
+  static constexpr int LDT = C + 4;               // fp32 A (row-major), T (column-major)
+  static constexpr int LDX = 20;                  // fp32 16x16 scratch of the solve
+  static constexpr int NB = C / 16;
   static constexpr int PARTS = kThreads / DK;  // threads per key channel
   static constexpr int RPP = C / PARTS;         // rows per part
   static_assert(kThreads % DK == 0 && C % PARTS == 0 && RPP >= 1, "prep split");
-  // The decayed operands and, once they are consumed, the triangular
-  // transform share storage.
-  static constexpr size_t kOps = 3 * static_cast<size_t>(C) * LDK * sizeof(OpT);
-  static constexpr size_t kTm = static_cast<size_t>(C) * LDA * sizeof(float);
-  static constexpr size_t kUnion = kOps > kTm ? kOps : kTm;
+  static constexpr size_t kOpRows = static_cast<size_t>(C) * LDK * sizeof(OpT);
+  static constexpr size_t kTm = static_cast<size_t>(C) * LDT * sizeof(float);
+  static constexpr size_t kKeT = static_cast<size_t>(DK) * LDC * sizeof(OpT);
+  static constexpr size_t al16(size_t x) { return (x + 15) / 16 * 16; }
+  static constexpr size_t kX = 4 * 16 * LDX * sizeof(float);
+  // Byte offsets.  Once A and P are done, Kh's storage holds T (column-major)
+  // and Qt's the solve scratch; Ke^T's holds A once Ke^T has been copied out.
+  static constexpr size_t oKt = 0;
+  static constexpr size_t oKh = al16(oKt + kOpRows);
+  static constexpr size_t oQt = al16(oKh + (kOpRows > kTm ? kOpRows : kTm));
+  static constexpr size_t oKe = al16(oQt + (kOpRows > kX ? kOpRows : kX));
+  static constexpr size_t oP = al16(oKe + (kKeT > kTm ? kKeT : kTm));
+  static constexpr size_t oX = oQt;
+  static constexpr size_t kBytes = al16(oP + static_cast<size_t>(C) * LDC * sizeof(OpT));
 };
 
 template <typename OpT, int DK, int C>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   using Sm = PrepSmem<OpT, DK, C>;
   using Blk = ChunkBlock<OpT, DK, C>;
-  constexpr int LDK = Sm::LDK, LDA = Sm::LDA, LDP = Sm::LDP;
+  constexpr int LDK = Sm::LDK, LDC = Sm::LDC, LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
   constexpr int PARTS = Sm::PARTS, RPP = Sm::RPP;
+  constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));  // elements per 16-byte piece
 
-  __shared__ __attribute__((aligned(16))) unsigned char u_raw[Sm::kUnion];
-  __shared__ float A_s[C * LDA];  // strict-lower beta-scaled key/key terms
-  __shared__ __attribute__((aligned(16))) OpT P_s[C * LDP];  // lower(Qt Kh^T)
+  __shared__ __attribute__((aligned(16))) unsigned char sm[Sm::kBytes];
   __shared__ float inv_nk[C], inv_nq[C], beta_s[C], gsc[C];
   __shared__ float gpart[PARTS][DK];
 
-  OpT* Kt_s = reinterpret_cast<OpT*>(u_raw);
-  OpT* Kh_s = Kt_s + C * LDK;
-  OpT* Qt_s = Kh_s + C * LDK;
-  float* T_s = reinterpret_cast<float*>(u_raw);  // after the operands are consumed
+  OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oKt);
+  OpT* Kh_s = reinterpret_cast<OpT*>(sm + Sm::oKh);
+  OpT* Qt_s = reinterpret_cast<OpT*>(sm + Sm::oQt);
+  OpT* KeT_s = reinterpret_cast<OpT*>(sm + Sm::oKe);
+  OpT* P_s = reinterpret_cast<OpT*>(sm + Sm::oP);
+  float* TT_s = reinterpret_cast<float*>(sm + Sm::oKh);  // T column-major: TT[s][r] = T[r][s]
+  float* A_s = reinterpret_cast<float*>(sm + Sm::oKe);   // A row-major
+  float* X_s = reinterpret_cast<float*>(sm + Sm::oX);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,28 +243,68 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   const int L = min(C, a.T - t0);
   const OpT* qg = static_cast<const OpT*>(a.q);
   const OpT* kg = static_cast<const OpT*>(a.k);
-  OpT* blk = reinterpret_cast<OpT*>(static_cast<unsigned char*>(a.ws) +
-                                    static_cast<size_t>(blockIdx.x) * Blk::kBytes);
+  unsigned char* blk_bytes =
+      static_cast<unsigned char*>(a.ws) + static_cast<size_t>(blockIdx.x) * Blk::kBytes;
+  const size_t qk_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_qk + hq;  // row t0
+  const size_t g_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_v + h;
 
-  // ---- per-row scalars: L2 norms, beta, scalar gate ----
-  for (int r = wave; r < C; r += kThreads / 64) {
-    float sk = 0.f, sq = 0.f;
-    const bool valid = r < L;
-    if (valid && a.l2norm) {
-      const size_t base = ((static_cast<size_t>(b) * a.T + t0 + r) * a.H_qk + hq) * DK;
-      for (int e = lane; e < DK; e += 64) {
-        float x = to_f32(kg[base + e]);
-        float y = to_f32(qg[base + e]);
-        sk += x * x;
-        sq += y * y;
+  // ---- 1. this thread's channel column: k, q (and g) for its rows ----
+  const int c = tid % DK;
+  const int part = tid / DK;
+  const int rlo = part * RPP;
+  float kc[RPP], qc[RPP], gc[RPP];
+#pragma unroll
+  for (int i = 0; i < RPP; ++i) {
+    const int r = rlo + i;
+    const int rr = r < L ? r : L - 1;  // rows past the end: load a valid row, then zero it
+    const float m = r < L ? 1.0f : 0.0f;
+    const size_t off = (qk_row0 + static_cast<size_t>(rr) * a.H_qk) * DK + c;
+    kc[i] = m * to_f32(kg[off]);
+    qc[i] = m * to_f32(qg[off]);
+    gc[i] = a.gate == GDR_GATE_CHANNEL
+                ? m * a.gate_in[(g_row0 + static_cast<size_t>(rr) * a.H_v) * DK + c]
+                : 0.0f;
+  }
+
+  // ---- 2. per-row L2 norms, beta, scalar gate (wave w: rows w, w+4, ...) ----
+  {
+    constexpr int RW = C / (kThreads / 64);  // rows per wave
+    constexpr int EPL = DK >= 64 ? DK / 64 : 1;  // elements per lane
+    float sk[RW], sq[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int r = wave + 4 * i;
+      sk[i] = sq[i] = 0.0f;
+      if (r < L && a.l2norm && lane * EPL < DK) {
+        const size_t off = (qk_row0 + static_cast<size_t>(r) * a.H_qk) * DK + lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float x = to_f32(kg[off + e]);
+          const float y = to_f32(qg[off + e]);
+          sk[i] += x * x;
+          sq[i] += y * y;
+        }
       }
-      sk = wave_sum(sk);
-      sq = wave_sum(sq);
     }
-    if (lane == 0) {
-      inv_nk[r] = a.l2norm ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
-      inv_nq[r] = a.l2norm ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f;
-      const size_t gi = (static_cast<size_t>(b) * a.T + t0 + r) * a.H_v + h;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      sk[i] = wave_sum(sk[i]);
+      sq[i] = wave_sum(sq[i]);
+    }
+    if (lane < RW) {
+      // lane i publishes row wave + 4 i (select the i-th entry without dynamic indexing)
+      float vk = 0.f, vq = 0.f;
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+        if (lane == i) {
+          vk = sk[i];
+          vq = sq[i];
+        }
+      const int r = wave + 4 * lane;
+      const bool valid = r < L;
+      inv_nk[r] = a.l2norm ? 1.0f / sqrtf(vk + kL2Eps) : 1.0f;
+      inv_nq[r] = a.l2norm ? 1.0f / sqrtf(vq + kL2Eps) : 1.0f;
+      const size_t gi = g_row0 + static_cast<size_t>(r) * a.H_v;
       beta_s[r] = valid ? sigmoidf(a.beta_logit[gi]) : 0.0f;
       float g = 0.0f;
       if (valid && a.gate == GDR_GATE_SCALAR) g = a.gate_in[gi];
@@ -195,55 +315,72 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   }
   __syncthreads();
 
-  // ---- per-channel log-decay prefix sums and decayed operands ----
-  const int c = tid % DK;
-  const int part = tid / DK;
-  const int rlo = part * RPP;
-  auto g_at = [&](int r) -> float {
-    if (r >= L) return 0.0f;
-    if (a.gate == GDR_GATE_CHANNEL)
-      return a.gate_in[((static_cast<size_t>(b) * a.T + t0 + r) * a.H_v + h) * DK + c];
-    return gsc[r];
-  };
+  // ---- 3. prefix sums and decayed operands ----
+  if (a.gate != GDR_GATE_CHANNEL) {
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) gc[i] = gsc[rlo + i];
+  }
   {
     float s = 0.f;
-    for (int r = rlo; r < rlo + RPP; ++r) s += g_at(r);
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) s += gc[i];
     gpart[part][c] = s;
   }
   __syncthreads();
   float gam = 0.f, total = 0.f;
+#pragma unroll
   for (int p = 0; p < PARTS; ++p) {
     const float x = gpart[p][c];
     if (p < part) gam += x;
     total += x;
   }
-  // gam is now Gamma just before row rlo; total is Gamma_L.
-  OpT* KeT_g = blk + Blk::kKeT + c * C;
-  for (int r = rlo; r < rlo + RPP; ++r) {
-    gam += g_at(r);
-    float kv = 0.f, qv = 0.f;
-    if (r < L) {
-      const size_t base = ((static_cast<size_t>(b) * a.T + t0 + r) * a.H_qk + hq) * DK + c;
-      kv = to_f32(kg[base]) * inv_nk[r];
-      qv = to_f32(qg[base]) * inv_nq[r];
+  // gam: Gamma just before row rlo; total: Gamma_L.
+  constexpr int KG = RPP < 4 ? RPP : 4;  // Ke^T values written per LDS store
+#pragma unroll
+  for (int i0 = 0; i0 < RPP; i0 += KG) {
+    OpT ke[KG];
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+      const int i = i0 + u;
+      const int r = rlo + i;
+      gam += gc[i];
+      const float kv = kc[i] * inv_nk[r];
+      const float qv = qc[i] * inv_nq[r];
+      const float e_pos = expf(gam);
+      const float e_neg = expf(-gam);
+      Kt_s[r * LDK + c] = from_f32<OpT>(kv * e_pos);
+      Kh_s[r * LDK + c] = from_f32<OpT>(kv * e_neg);
+      Qt_s[r * LDK + c] = from_f32<OpT>(qv * e_pos);
+      ke[u] = from_f32<OpT>(kv * expf(total - gam));
     }
-    const float e_pos = expf(gam), e_neg = expf(-gam);
-    const OpT kt = from_f32<OpT>(kv * e_pos);
-    const OpT qt = from_f32<OpT>(qv * e_pos);
-    Kt_s[r * LDK + c] = kt;
-    Kh_s[r * LDK + c] = from_f32<OpT>(kv * e_neg);
-    Qt_s[r * LDK + c] = qt;
-    blk[Blk::kKt + r * DK + c] = kt;
-    blk[Blk::kQt + r * DK + c] = qt;
-    KeT_g[r] = from_f32<OpT>(kv * expf(total - gam));
+    OpT* dst = KeT_s + c * LDC + rlo + i0;
+#pragma unroll
+    for (int u = 0; u < KG; ++u) dst[u] = ke[u];
   }
   if (part == 0)
-    reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(blk) + Blk::kGammaByte)[c] =
-        expf(total);
+    reinterpret_cast<float*>(blk_bytes + Blk::kGammaByte)[c] = expf(total);
   __syncthreads();
 
-  // ---- A = strict_lower(diag(beta) Kt Kh^T) and P = lower(Qt Kh^T) by MFMA ----
-  constexpr int NB = C / 16;
+  // ---- copy Kt, Qt, Ke^T out (16-byte pieces); Ke^T's storage is reused by A ----
+  {
+    constexpr int PR = DK / VPER;  // pieces per row of Kt / Qt
+    constexpr int PC = C / VPER;   // pieces per row of Ke^T
+    uint4* out = reinterpret_cast<uint4*>(blk_bytes);
+    for (int p = tid; p < C * PR; p += kThreads) {
+      const int r = p / PR, q = p % PR;
+      const int qs = q ^ swz_key(r, PR);
+      out[(Blk::kKt + r * DK) / VPER + qs] = *reinterpret_cast<const uint4*>(Kt_s + r * LDK + q * VPER);
+      out[(Blk::kQt + r * DK) / VPER + qs] = *reinterpret_cast<const uint4*>(Qt_s + r * LDK + q * VPER);
+    }
+    for (int p = tid; p < DK * PC; p += kThreads) {
+      const int r = p / PC, q = p % PC;
+      out[(Blk::kKeT + r * C) / VPER + (q ^ swz_key(r, PC))] =
+          *reinterpret_cast<const uint4*>(KeT_s + r * LDC + q * VPER);
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. A = strict_lower(diag(beta) Kt Kh^T) and P = lower(Qt Kh^T) ----
   constexpr int NL = NB * (NB + 1) / 2;  // lower-triangular 16x16 tiles
   for (int job = wave; job < 2 * NL; job += kThreads / 64) {
     const int tl = job % NL;
@@ -258,84 +395,182 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * R + 4 * (lane >> 4) + e;
       if (isP)
-        P_s[row * LDP + col] = from_f32<OpT>(row >= col ? acc[e] : 0.0f);
+        P_s[row * LDC + col] = from_f32<OpT>(row >= col ? acc[e] : 0.0f);
       else
-        A_s[row * LDA + col] = row > col ? beta_s[row] * acc[e] : 0.0f;
+        A_s[row * LDT + col] = row > col ? beta_s[row] * acc[e] : 0.0f;
     }
   }
-  // Upper tiles of P are zero.
-  for (int idx = tid; idx < C * C; idx += kThreads) {
+  for (int idx = tid; idx < C * C; idx += kThreads) {  // upper tiles of P are zero
     const int row = idx / C, col = idx % C;
-    if ((row >> 4) < (col >> 4)) P_s[row * LDP + col] = from_f32<OpT>(0.0f);
+    if ((row >> 4) < (col >> 4)) P_s[row * LDC + col] = from_f32<OpT>(0.0f);
   }
-  __syncthreads();  // Kt/Kh/Qt are dead from here; their storage becomes T_s
+  __syncthreads();  // Kh is dead: its storage becomes T (column-major)
 
-  // ---- (I + A)^-1 by forward substitution, one column per thread ----
-  if (tid < C) {
-    const int s = tid;
-    for (int r = 0; r < s; ++r) T_s[r * LDA + s] = 0.0f;
-    T_s[s * LDA + s] = 1.0f;
-    for (int r = s + 1; r < C; ++r) {
+  // ---- 5a. diagonal 16x16 blocks of (I + A)^-1: lane = column ----
+  if (wave < NB && lane < 16) {
+    const int o = 16 * wave;
+    const int s = lane;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = r == s ? 1.0f : 0.0f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
       float acc = 0.0f;
-      for (int m = s; m < r; ++m) acc += A_s[r * LDA + m] * T_s[m * LDA + s];
-      T_s[r * LDA + s] = -acc;
+#pragma unroll
+      for (int m = 0; m < r; ++m) acc += A_s[(o + r) * LDT + o + m] * x[m];
+      if (r > s) x[r] = -acc;
     }
+    float* col = TT_s + (o + s) * LDT + o;
+#pragma unroll
+    for (int r = 0; r < 16; r += 4)
+      *reinterpret_cast<float4*>(col + r) = make_float4(x[r], x[r + 1], x[r + 2], x[r + 3]);
   }
   __syncthreads();
 
-  // ---- write Tb = T diag(beta) and P to the workspace ----
-  OpT* Tb_g = blk + Blk::kTb;
-  OpT* P_g = blk + Blk::kP;
-  for (int idx = tid; idx < C * C; idx += kThreads) {
-    const int row = idx / C, col = idx % C;
-    Tb_g[idx] = from_f32<OpT>(row >= col ? T_s[row * LDA + col] * beta_s[col] : 0.0f);
-    P_g[idx] = P_s[row * LDP + col];
+  // ---- 5b. off-diagonal blocks, by distance from the diagonal ----
+#pragma unroll
+  for (int d = 1; d < NB; ++d) {
+    const int jobs = NB - d;
+    const int j = wave, i = wave + d;
+    float* Xw = X_s + wave * 16 * LDX;  // column-major 16x16: Xw[c][r]
+    if (wave < jobs) {
+      // X = sum_{k=j}^{i-1} A_ik T_kj
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = j; kb < i; ++kb) {
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const float xa = A_s[(16 * i + (lane & 15)) * LDT + 16 * kb + k0 + (lane >> 4)];
+          const float zb = TT_s[(16 * j + (lane & 15)) * LDT + 16 * kb + k0 + (lane >> 4)];
+          acc = mfma_f32x4(xa, zb, acc);
+        }
+      }
+      *reinterpret_cast<float4*>(Xw + (lane & 15) * LDX + 4 * (lane >> 4)) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+    if (wave < jobs) {
+      // T_ij = -T_ii X
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        const float xa = TT_s[(16 * i + k0 + (lane >> 4)) * LDT + 16 * i + (lane & 15)];
+        const float zb = Xw[(lane & 15) * LDX + k0 + (lane >> 4)];
+        acc = mfma_f32x4(xa, zb, acc);
+      }
+      *reinterpret_cast<float4*>(TT_s + (16 * j + (lane & 15)) * LDT + 16 * i + 4 * (lane >> 4)) =
+          make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
+    }
+    __syncthreads();
+  }
+
+  // ---- 6. Tb = T diag(beta) and P out, 16-byte pieces ----
+  {
+    constexpr int PC = C / VPER;
+    uint4* out = reinterpret_cast<uint4*>(blk_bytes);
+    for (int p = tid; p < C * PC; p += kThreads) {
+      const int r = p / PC, s0 = (p % PC) * VPER;
+      OpT v[VPER];
+#pragma unroll
+      for (int u = 0; u < VPER; ++u) {
+        const int s = s0 + u;
+        v[u] = from_f32<OpT>(r >= s ? TT_s[s * LDT + r] * beta_s[s] : 0.0f);
+      }
+      const int qs = (p % PC) ^ swz_key(r, PC);
+      out[(Blk::kTb + r * C) / VPER + qs] = *reinterpret_cast<const uint4*>(v);
+      out[(Blk::kP + r * C) / VPER + qs] = *reinterpret_cast<const uint4*>(P_s + r * LDC + s0);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // chunk_carry
+//
+// One workgroup per (b, h, slice of DVS state columns); the slice of S lives in
+// MFMA accumulators for the whole sequence.  Each chunk's workspace block is
+// brought into LDS by direct-to-LDS loads (global_load_lds_dwordx4), issued
+// one chunk ahead into the other half of a double buffer, so no registers hold
+// the prefetch and the copy overlaps the current chunk's arithmetic.  The
+// block is stored XOR-swizzled (see swz_key), so the straight copy lands in a
+// layout whose MFMA operand reads are free of LDS bank conflicts.
+// Per chunk, three barriers:
+//   [B1]  S^T (operand type) written; this chunk's block has landed
+//   c:    R = V - Kt S (to LDS, transposed), O = Qt S (registers)      [B2]
+//   d:    U = Tb R (to LDS, transposed)                                  [B3]
+//   e:    O += P U -> o;  S = e^Gamma_L . S + Ke^T U
 // ---------------------------------------------------------------------------
-template <typename OpT, int DK, int DVS, int C>
+template <typename OpT, int DK, int DVS, int C, int NBUF>
 struct CarryShape {
   using Blk = ChunkBlock<OpT, DK, C>;
   static constexpr int P = pad_of<OpT>();
-  static constexpr int LDK = DK + P;  // rows of Kt, Qt, St
-  static constexpr int LDC = C + P;   // rows of KeT, Tb, P, Rt, Ut
-  static constexpr int LDV = DVS + 1;
+  static constexpr int LDK = DK + P;  // rows of St
+  static constexpr int LDC = C + P;   // rows of Rt, Ut
   static constexpr int NW = kThreads / 64;
   static constexpr int NST = (DK / 16) * (DVS / 16);  // state tiles
   static constexpr int SPW = (NST + NW - 1) / NW;      // state tiles per wave
   static constexpr int NOT = (C / 16) * (DVS / 16);   // output tiles
   static constexpr int OPW = (NOT + NW - 1) / NW;
-  static constexpr int kPieces = static_cast<int>(Blk::kBytes / 16);  // 16-byte pieces
-  static constexpr int kPF = (kPieces + kThreads - 1) / kThreads;
-  static constexpr int kVPer = 16 / static_cast<int>(sizeof(OpT));   // elements per piece
-  static constexpr int kVPieces = C * DVS / kVPer;
-  static constexpr int kVPF = (kVPieces + kThreads - 1) / kThreads;
-  static constexpr size_t kSmem =
-      sizeof(OpT) * (2 * C * LDK + DK * LDC + 2 * C * LDC + DVS * LDK + 2 * DVS * LDC) +
-      sizeof(float) * (C * LDV + DK);
+  static constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));
+  static constexpr int kPieces = static_cast<int>(Blk::kBytes / 16);  // block, 16-byte pieces
+  static constexpr int kVRowPieces = DVS / VPER;                      // V row of the slice
+  static constexpr int kVPieces = C * kVRowPieces;
+  static constexpr size_t kBuf = Blk::kBytes;
+  static constexpr size_t kVBuf = static_cast<size_t>(C) * DVS * sizeof(OpT);
+  static constexpr size_t kSmem = NBUF * (kBuf + kVBuf) +
+                                  sizeof(OpT) * (DVS * LDK + 2 * DVS * LDC);
 };
 
-template <typename OpT, int DK, int DVS, int C>
-__global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
-  using Sh = CarryShape<OpT, DK, DVS, C>;
+// Direct-to-LDS copy of chunk nn's workspace block and V slice into one
+// buffer of the carry kernel.  Wave w moves 16-byte pieces w*64 + 256 j + lane
+// (lanes past the end idle); the hardware writes lane i's piece at LDS
+// base + 16 i, so each wave instruction fills 1 KiB of the buffer in order.
+template <typename OpT, int DK, int DVS, int C, int NBUF>
+__device__ __forceinline__ void carry_issue(const PrefillArgs& a, const unsigned char* ws_head,
+                                            unsigned char* dst, OpT* vdst_e, int nn, int b,
+                                            int h, int jb, int wave, int lane, int part,
+                                            int parts) {
+  using Sh = CarryShape<OpT, DK, DVS, C, NBUF>;
   using Blk = typename Sh::Blk;
-  constexpr int LDK = Sh::LDK, LDC = Sh::LDC, LDV = Sh::LDV;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  // Part `part` of `parts` moves every parts-th 256-piece row of the block, so
+  // the copy can be spread over the phases of the current chunk.
+  const unsigned char* src = ws_head + static_cast<size_t>(nn) * Blk::kBytes;
+  for (int base = wave * 64 + part * kThreads; base < Sh::kPieces; base += parts * kThreads) {
+    const int piece = base + lane;
+    if (piece < Sh::kPieces)
+      __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(piece) * 16,
+                                       (lds_ptr)(dst + base * 16), 16, 0, 0);
+  }
+  if (part != parts - 1) return;
+  const int t0 = nn * C;
+  const OpT* vg = static_cast<const OpT*>(a.v);
+  unsigned char* vdst = reinterpret_cast<unsigned char*>(vdst_e);
+  for (int base = wave * 64; base < Sh::kVPieces; base += kThreads) {
+    const int piece = base + lane;
+    if (piece < Sh::kVPieces) {
+      const int r = piece / Sh::kVRowPieces;
+      const int col = (piece % Sh::kVRowPieces) * Sh::VPER;
+      const int t = min(t0 + r, a.T - 1);  // rows past the end are masked when read
+      const OpT* p = vg + ((static_cast<size_t>(b) * a.T + t) * a.H_v + h) * a.dv + jb + col;
+      __builtin_amdgcn_global_load_lds(p, (lds_ptr)(vdst + base * 16), 16, 0, 0);
+    }
+  }
+}
+
+template <typename OpT, int DK, int DVS, int C, int NBUF>
+__global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
+  using Sh = CarryShape<OpT, DK, DVS, C, NBUF>;
+  using Blk = typename Sh::Blk;
+  constexpr int LDK = Sh::LDK, LDC = Sh::LDC;
   constexpr int SPW = Sh::SPW, OPW = Sh::OPW, NST = Sh::NST, NOT = Sh::NOT;
   constexpr int DVT = DVS / 16;
+  constexpr int PPR_K = DK * static_cast<int>(sizeof(OpT)) / 16;  // pieces per row, [.][DK]
+  constexpr int PPR_C = C * static_cast<int>(sizeof(OpT)) / 16;   // pieces per row, [.][C]
 
-  __shared__ __attribute__((aligned(16))) OpT Kt_s[C * LDK];
-  __shared__ __attribute__((aligned(16))) OpT Qt_s[C * LDK];
-  __shared__ __attribute__((aligned(16))) OpT KeT_s[DK * LDC];
-  __shared__ __attribute__((aligned(16))) OpT Tb_s[C * LDC];
-  __shared__ __attribute__((aligned(16))) OpT P_s[C * LDC];
+  __shared__ __attribute__((aligned(16))) unsigned char bufs[NBUF][Sh::kBuf];
+  __shared__ __attribute__((aligned(16))) OpT vbufs[NBUF][C * DVS];
   __shared__ __attribute__((aligned(16))) OpT St_s[DVS * LDK];
   __shared__ __attribute__((aligned(16))) OpT Rt_s[DVS * LDC];
   __shared__ __attribute__((aligned(16))) OpT Ut_s[DVS * LDC];
-  __shared__ float V_s[C * LDV];
-  __shared__ __attribute__((aligned(16))) float gam_s[DK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -358,7 +593,6 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
   const size_t st_off = static_cast<size_t>(bh) * DK * a.dv;
   const unsigned char* ws_head =
       static_cast<const unsigned char*>(a.ws) + static_cast<size_t>(bh) * NC * Blk::kBytes;
-  const OpT* vg = static_cast<const OpT*>(a.v);
   OpT* og = static_cast<OpT*>(a.o);
 
   // ---- state tiles owned by this wave, in accumulator layout ----
@@ -378,77 +612,41 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- prefetch registers for one chunk block and one V slice ----
-  uint4 pf[Sh::kPF];
-  uint4 vpf[Sh::kVPF];
-  auto fetch = [&](int nn) __attribute__((always_inline)) {
-    const uint4* src = reinterpret_cast<const uint4*>(ws_head + static_cast<size_t>(nn) * Blk::kBytes);
+  // The outputs of chunk nn are stored at the start of chunk nn+1, right after
+  // its wait for the block copies: vmcnt also counts stores, so storing them
+  // earlier would make that wait sit out their write acknowledgements.
+  f32x4 opend[OPW];
+  int t0_pend = 0, L_pend = 0;
+  auto store_pending = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < Sh::kPF; ++i) {
-      const int piece = tid + i * kThreads;
-      if (piece < Sh::kPieces) pf[i] = src[piece];
-    }
-    const int t0 = nn * C;
+    for (int i = 0; i < OPW; ++i) {
+      const int t = wave * OPW + i;
+      if (t < NOT) {
+        const int R = t / DVT, J = t % DVT;
 #pragma unroll
-    for (int i = 0; i < Sh::kVPF; ++i) {
-      const int piece = tid + i * kThreads;
-      vpf[i] = uint4{0u, 0u, 0u, 0u};
-      if (piece < Sh::kVPieces) {
-        const int r = piece / (DVS / Sh::kVPer);
-        const int col = (piece % (DVS / Sh::kVPer)) * Sh::kVPer;
-        if (t0 + r < a.T)
-          vpf[i] = *reinterpret_cast<const uint4*>(
-              vg + ((static_cast<size_t>(b) * a.T + t0 + r) * a.H_v + h) * a.dv + jb + col);
-      }
-    }
-  };
-  auto stage = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < Sh::kPF; ++i) {
-      const int piece = tid + i * kThreads;
-      if (piece >= Sh::kPieces) continue;
-      const int byte = piece * 16;
-      unsigned char* dst;
-      if (byte < static_cast<int>(Blk::kGammaByte)) {
-        const int e = byte / static_cast<int>(sizeof(OpT));
-        if (e < Blk::kQt) {
-          dst = reinterpret_cast<unsigned char*>(Kt_s + (e / DK) * LDK + e % DK);
-        } else if (e < Blk::kKeT) {
-          const int f = e - Blk::kQt;
-          dst = reinterpret_cast<unsigned char*>(Qt_s + (f / DK) * LDK + f % DK);
-        } else if (e < Blk::kTb) {
-          const int f = e - Blk::kKeT;
-          dst = reinterpret_cast<unsigned char*>(KeT_s + (f / C) * LDC + f % C);
-        } else if (e < Blk::kP) {
-          const int f = e - Blk::kTb;
-          dst = reinterpret_cast<unsigned char*>(Tb_s + (f / C) * LDC + f % C);
-        } else {
-          const int f = e - Blk::kP;
-          dst = reinterpret_cast<unsigned char*>(P_s + (f / C) * LDC + f % C);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + 4 * (lane >> 4) + e;
+          if (r < L_pend)
+            og[((static_cast<size_t>(b) * a.T + t0_pend + r) * a.H_v + h) * a.dv + jb + 16 * J +
+               (lane & 15)] = from_f32<OpT>(a.scale * opend[i][e]);
         }
-      } else {
-        const int f = (byte - static_cast<int>(Blk::kGammaByte)) / 4;
-        if (f >= DK) continue;  // tail padding of the block
-        dst = reinterpret_cast<unsigned char*>(gam_s + f);
       }
-      *reinterpret_cast<uint4*>(dst) = pf[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Sh::kVPF; ++i) {
-      const int piece = tid + i * kThreads;
-      if (piece >= Sh::kVPieces) continue;
-      const int r = piece / (DVS / Sh::kVPer);
-      const int col = (piece % (DVS / Sh::kVPer)) * Sh::kVPer;
-      const OpT* e = reinterpret_cast<const OpT*>(&vpf[i]);
-#pragma unroll
-      for (int u = 0; u < Sh::kVPer; ++u) V_s[r * LDV + col + u] = to_f32(e[u]);
     }
   };
 
-  if (NC > 0) fetch(0);
+  carry_issue<OpT, DK, DVS, C, NBUF>(a, ws_head, bufs[0], vbufs[0], 0, b, h, jb, wave, lane, 0,
+                                     1);
   for (int nn = 0; nn < NC; ++nn) {
     const int t0 = nn * C;
     const int L = min(C, a.T - t0);
+    const int cur = NBUF == 2 ? (nn & 1) : 0;
+    const OpT* Kt_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kKt;
+    const OpT* Qt_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kQt;
+    const OpT* KeT_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kKeT;
+    const OpT* Tb_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kTb;
+    const OpT* P_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kP;
+    const float* gam_b = reinterpret_cast<const float*>(bufs[cur] + Blk::kGammaByte);
+    const OpT* V_b = vbufs[cur];
 
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll
@@ -460,9 +658,13 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
         store_tile_t<OpT>(St_s, LDK, 16 * J, 16 * I, v, lane);
       }
     }
-    stage();
-    __syncthreads();
-    if (nn + 1 < NC) fetch(nn + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of chunk nn landed
+    __syncthreads();                                     // [B1] ... and everyone else's
+    // The next chunk's copy overlaps this chunk's arithmetic.
+    if (NBUF == 2 && nn + 1 < NC)
+      carry_issue<OpT, DK, DVS, C, NBUF>(a, ws_head, bufs[cur ^ 1], vbufs[cur ^ 1], nn + 1, b, h,
+                                         jb, wave, lane, 0, 1);
+    if (nn > 0) store_pending();
 
     // R = V - Kt S  (stored transposed),  O = Qt S (kept in registers).
     f32x4 oacc[OPW];
@@ -473,16 +675,19 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
       if (t < NOT) {
         const int R = t / DVT, J = t % DVT;
         f32x4 ks = {0.f, 0.f, 0.f, 0.f};
-        ks = mma_xzt<OpT, DK>(Kt_s, LDK, 16 * R, St_s, LDK, 16 * J, ks, lane);
-        oacc[i] = mma_xzt<OpT, DK>(Qt_s, LDK, 16 * R, St_s, LDK, 16 * J, oacc[i], lane);
+        ks = mma_swz<OpT, DK>(Kt_b, PPR_K, 16 * R, St_s, LDK, 16 * J, ks, lane);
+        oacc[i] = mma_swz<OpT, DK>(Qt_b, PPR_K, 16 * R, St_s, LDK, 16 * J, oacc[i], lane);
         float rv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          rv[e] = V_s[(16 * R + 4 * (lane >> 4) + e) * LDV + 16 * J + (lane & 15)] - ks[e];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + 4 * (lane >> 4) + e;
+          const float vv = r < L ? to_f32(V_b[r * DVS + 16 * J + (lane & 15)]) : 0.0f;
+          rv[e] = vv - ks[e];
+        }
         store_tile_t<OpT>(Rt_s, LDC, 16 * J, 16 * R, rv, lane);
       }
     }
-    __syncthreads();
+    __syncthreads();  // [B2]
 
     // U = Tb R  (stored transposed).
 #pragma unroll
@@ -491,29 +696,24 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
       if (t < NOT) {
         const int R = t / DVT, J = t % DVT;
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
-        u = mma_xzt<OpT, C>(Tb_s, LDC, 16 * R, Rt_s, LDC, 16 * J, u, lane);
+        u = mma_swz<OpT, C>(Tb_b, PPR_C, 16 * R, Rt_s, LDC, 16 * J, u, lane);
         float uv[4] = {u[0], u[1], u[2], u[3]};
         store_tile_t<OpT>(Ut_s, LDC, 16 * J, 16 * R, uv, lane);
       }
     }
-    __syncthreads();
+    __syncthreads();  // [B3]
 
-    // O = scale (Qt S + P U) -> o rows of this chunk.
+    // O = Qt S + P U, stored (times scale) at the start of the next chunk.
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
       const int t = wave * OPW + i;
       if (t < NOT) {
         const int R = t / DVT, J = t % DVT;
-        oacc[i] = mma_xzt<OpT, C>(P_s, LDC, 16 * R, Ut_s, LDC, 16 * J, oacc[i], lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * R + 4 * (lane >> 4) + e;
-          if (r < L)
-            og[((static_cast<size_t>(b) * a.T + t0 + r) * a.H_v + h) * a.dv + jb + 16 * J +
-               (lane & 15)] = from_f32<OpT>(a.scale * oacc[i][e]);
-        }
+        opend[i] = mma_swz<OpT, C>(P_b, PPR_C, 16 * R, Ut_s, LDC, 16 * J, oacc[i], lane);
       }
     }
+    t0_pend = t0;
+    L_pend = L;
     // S = diag(e^Gamma_L) S + Ke^T U.
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -521,12 +721,18 @@ __global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
       if (t < NST) {
         const int I = t / DVT, J = t % DVT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[i][e] *= gam_s[16 * I + 4 * (lane >> 4) + e];
-        sacc[i] = mma_xzt<OpT, C>(KeT_s, LDC, 16 * I, Ut_s, LDC, 16 * J, sacc[i], lane);
+        for (int e = 0; e < 4; ++e) sacc[i][e] *= gam_b[16 * I + 4 * (lane >> 4) + e];
+        sacc[i] = mma_swz<OpT, C>(KeT_b, PPR_C, 16 * I, Ut_s, LDC, 16 * J, sacc[i], lane);
       }
     }
-    __syncthreads();
+    if (NBUF == 1 && nn + 1 < NC) {
+      __syncthreads();  // single buffer: everyone is done with it before it is refilled
+      carry_issue<OpT, DK, DVS, C, NBUF>(a, ws_head, bufs[0], vbufs[0], nn + 1, b, h, jb, wave,
+                                         lane, 0, 1);
+    }
   }
+
+  if (NC > 0) store_pending();
 
   // ---- final state ----
 #pragma unroll
@@ -574,37 +780,45 @@ size_t block_bytes_rt(int dk, int chunk) {
 
 constexpr size_t kSmemLimit = 160 * 1024;
 
-// Widest state slice whose carry workgroup fits in LDS and that still gives
-// at least `want` workgroups.
-template <typename OpT, int DK, int C>
-int carry_slice(int units, int dv) {
-  constexpr int cand[4] = {128, 64, 32, 16};
-  int best = 0;
-  for (int dvs : cand) {
-    if (dvs > dv) continue;
-    size_t smem = 0;
-    switch (dvs) {
-      case 128: smem = CarryShape<OpT, DK, 128, C>::kSmem; break;
-      case 64: smem = CarryShape<OpT, DK, 64, C>::kSmem; break;
-      case 32: smem = CarryShape<OpT, DK, 32, C>::kSmem; break;
-      default: smem = CarryShape<OpT, DK, 16, C>::kSmem; break;
-    }
-    if (smem > kSmemLimit) continue;
-    best = dvs;
-    if (static_cast<long>(units) * (dv / dvs) >= 256) break;
-  }
-  return best;
+template <typename OpT, int DK, int DVS, int C, int NBUF>
+constexpr bool carry_fits() {
+  return CarryShape<OpT, DK, DVS, C, NBUF>::kSmem <= kSmemLimit;
 }
 
-template <typename OpT, int DK, int DVS, int C>
+template <typename OpT, int DK, int DVS, int C, int NBUF>
 hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (CarryShape<OpT, DK, DVS, C>::kSmem > kSmemLimit) {
+  if constexpr (!carry_fits<OpT, DK, DVS, C, NBUF>()) {
     return hipErrorInvalidConfiguration;
   } else {
     const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
-    hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C>), dim3(grid), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, NBUF>), dim3(grid), dim3(kThreads),
+                       0, stream, a);
     return hipGetLastError();
+  }
+}
+
+// Slice width: the narrowest that still keeps the (b, h, slice) workgroups
+// within one per CU (each takes most of a CU's LDS), at least 16 columns;
+// the chunk block is double-buffered when that fits in LDS.
+template <typename OpT, int DK, int DVS, int C>
+hipError_t launch_carry_buf(const PrefillArgs& a, hipStream_t stream) {
+  if constexpr (carry_fits<OpT, DK, DVS, C, 2>())
+    return launch_carry<OpT, DK, DVS, C, 2>(a, stream);
+  else
+    return launch_carry<OpT, DK, DVS, C, 1>(a, stream);
+}
+
+template <typename OpT, int DK, int C>
+hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
+  const long units = static_cast<long>(a.B) * a.H_v;
+  int dvs = 16;
+  while (dvs < a.dv && units * (a.dv / dvs) > 256) dvs *= 2;
+  if (dvs > a.dv) dvs = a.dv;
+  switch (dvs) {
+    case 16: return launch_carry_buf<OpT, DK, 16, C>(a, stream);
+    case 32: return launch_carry_buf<OpT, DK, 32, C>(a, stream);
+    case 64: return launch_carry_buf<OpT, DK, 64, C>(a, stream);
+    default: return launch_carry_buf<OpT, DK, 128, C>(a, stream);
   }
 }
 
@@ -616,14 +830,7 @@ hipError_t launch_dk_c(const PrefillArgs& a, hipStream_t stream) {
                      a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int dvs = carry_slice<OpT, DK, C>(a.B * a.H_v, a.dv);
-  switch (dvs) {
-    case 128: return launch_carry<OpT, DK, 128, C>(a, stream);
-    case 64: return launch_carry<OpT, DK, 64, C>(a, stream);
-    case 32: return launch_carry<OpT, DK, 32, C>(a, stream);
-    case 16: return launch_carry<OpT, DK, 16, C>(a, stream);
-    default: return hipErrorInvalidConfiguration;
-  }
+  return launch_carry_any<OpT, DK, C>(a, stream);
 }
 
 template <typename OpT, int DK>

@@ -504,7 +504,9 @@ struct CarryShape {
   static constexpr int P = pad_of<OpT>();
   static constexpr int LDK = DK + P;  // rows of St
   static constexpr int LDC = C + P;   // rows of Rt, Ut
-  static constexpr int NW = kThreads / 64;
+  // Eight waves (two per SIMD) once a slice has enough tiles to share out.
+  static constexpr int NT = DVS >= 32 ? 512 : 256;
+  static constexpr int NW = NT / 64;
   static constexpr int NST = (DK / 16) * (DVS / 16);  // state tiles
   static constexpr int SPW = (NST + NW - 1) / NW;      // state tiles per wave
   static constexpr int NOT = (C / 16) * (DVS / 16);   // output tiles
@@ -520,7 +522,7 @@ struct CarryShape {
 };
 
 // Direct-to-LDS copy of chunk nn's workspace block and V slice into one
-// buffer of the carry kernel.  Wave w moves 16-byte pieces w*64 + 256 j + lane
+// buffer of the carry kernel.  Wave w moves 16-byte pieces w*64 + NT j + lane
 // (lanes past the end idle); the hardware writes lane i's piece at LDS
 // base + 16 i, so each wave instruction fills 1 KiB of the buffer in order.
 template <typename OpT, int DK, int DVS, int C, int NBUF>
@@ -534,7 +536,7 @@ __device__ __forceinline__ void carry_issue(const PrefillArgs& a, const unsigned
   // Part `part` of `parts` moves every parts-th 256-piece row of the block, so
   // the copy can be spread over the phases of the current chunk.
   const unsigned char* src = ws_head + static_cast<size_t>(nn) * Blk::kBytes;
-  for (int base = wave * 64 + part * kThreads; base < Sh::kPieces; base += parts * kThreads) {
+  for (int base = wave * 64 + part * Sh::NT; base < Sh::kPieces; base += parts * Sh::NT) {
     const int piece = base + lane;
     if (piece < Sh::kPieces)
       __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(piece) * 16,
@@ -544,7 +546,7 @@ __device__ __forceinline__ void carry_issue(const PrefillArgs& a, const unsigned
   const int t0 = nn * C;
   const OpT* vg = static_cast<const OpT*>(a.v);
   unsigned char* vdst = reinterpret_cast<unsigned char*>(vdst_e);
-  for (int base = wave * 64; base < Sh::kVPieces; base += kThreads) {
+  for (int base = wave * 64; base < Sh::kVPieces; base += Sh::NT) {
     const int piece = base + lane;
     if (piece < Sh::kVPieces) {
       const int r = piece / Sh::kVRowPieces;
@@ -557,7 +559,8 @@ __device__ __forceinline__ void carry_issue(const PrefillArgs& a, const unsigned
 }
 
 template <typename OpT, int DK, int DVS, int C, int NBUF>
-__global__ __launch_bounds__(kThreads) void chunk_carry_kernel(PrefillArgs a) {
+__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, NBUF>::NT)) void chunk_carry_kernel(
+    PrefillArgs a) {
   using Sh = CarryShape<OpT, DK, DVS, C, NBUF>;
   using Blk = typename Sh::Blk;
   constexpr int LDK = Sh::LDK, LDC = Sh::LDC;
@@ -791,15 +794,16 @@ hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
     return hipErrorInvalidConfiguration;
   } else {
     const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
-    hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, NBUF>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, NBUF>), dim3(grid),
+                       dim3(CarryShape<OpT, DK, DVS, C, NBUF>::NT),
                        0, stream, a);
     return hipGetLastError();
   }
 }
 
-// Slice width: the narrowest that still keeps the (b, h, slice) workgroups
-// within one per CU (each takes most of a CU's LDS), at least 16 columns;
-// the chunk block is double-buffered when that fits in LDS.
+// Slice width: the narrowest (from 32 columns, 8 waves) that keeps the
+// (b, h, slice) workgroups within one per CU, since each takes most of a CU's
+// LDS; the chunk block is double-buffered when that fits in LDS.
 template <typename OpT, int DK, int DVS, int C>
 hipError_t launch_carry_buf(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (carry_fits<OpT, DK, DVS, C, 2>())
@@ -811,7 +815,7 @@ hipError_t launch_carry_buf(const PrefillArgs& a, hipStream_t stream) {
 template <typename OpT, int DK, int C>
 hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
   const long units = static_cast<long>(a.B) * a.H_v;
-  int dvs = 16;
+  int dvs = a.dv < 32 ? a.dv : 32;
   while (dvs < a.dv && units * (a.dv / dvs) > 256) dvs *= 2;
   if (dvs > a.dv) dvs = a.dv;
   switch (dvs) {

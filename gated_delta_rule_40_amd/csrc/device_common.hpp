@@ -61,6 +61,16 @@ __device__ __forceinline__ void store4(T* __restrict__ p, float a, float b, floa
   }
 }
 
+// Store 4 io-dtype values held as T (8 or 16 bytes, aligned).
+template <typename T>
+__device__ __forceinline__ void store_vec4(T* __restrict__ p, const T (&v)[4]) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(v);
+  } else {
+    *reinterpret_cast<uint2*>(p) = *reinterpret_cast<const uint2*>(v);
+  }
+}
+
 // Sum over the 64 lanes of a wave; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -190,9 +190,13 @@ struct PrepSmem {
   static constexpr int LDT = C + 4;               // fp32 A (row-major), T (column-major)
   static constexpr int LDX = 20;                  // fp32 16x16 scratch of the solve
   static constexpr int NB = C / 16;
-  static constexpr int PARTS = kThreads / DK;  // threads per key channel
-  static constexpr int RPP = C / PARTS;         // rows per part
-  static_assert(kThreads % DK == 0 && C % PARTS == 0 && RPP >= 1, "prep split");
+  // Channel phase: a thread owns a quad of key channels and RPP consecutive
+  // rows (one row part); the NQ threads of a part are consecutive lanes.
+  static constexpr int NQ = DK / 4;                                    // channel quads
+  static constexpr int PARTS = (4 * kThreads / DK) < C ? 4 * kThreads / DK : C;
+  static constexpr int NTA = PARTS * NQ;                               // active threads
+  static constexpr int RPP = C / PARTS;                                // rows per part
+  static_assert(NTA <= kThreads && NTA % 64 == 0 && C % PARTS == 0, "prep split");
   static constexpr size_t kOpRows = static_cast<size_t>(C) * LDK * sizeof(OpT);
   static constexpr size_t kTm = static_cast<size_t>(C) * LDT * sizeof(float);
   static constexpr size_t kKeT = static_cast<size_t>(DK) * LDC * sizeof(OpT);
@@ -206,7 +210,11 @@ struct PrepSmem {
   static constexpr size_t oKe = al16(oQt + (kOpRows > kX ? kOpRows : kX));
   static constexpr size_t oP = al16(oKe + (kKeT > kTm ? kKeT : kTm));
   static constexpr size_t oX = oQt;
-  static constexpr size_t kBytes = al16(oP + static_cast<size_t>(C) * LDC * sizeof(OpT));
+  // The per-part channel sums of the prefix phase live where P goes later.
+  static constexpr size_t kP = static_cast<size_t>(C) * LDC * sizeof(OpT);
+  static constexpr size_t kG = static_cast<size_t>(PARTS) * DK * sizeof(float);
+  static constexpr size_t oG = oP;
+  static constexpr size_t kBytes = al16(oP + (kP > kG ? kP : kG));
 };
 
 template <typename OpT, int DK, int C>
@@ -218,8 +226,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));  // elements per 16-byte piece
 
   __shared__ __attribute__((aligned(16))) unsigned char sm[Sm::kBytes];
-  __shared__ float inv_nk[C], inv_nq[C], beta_s[C], gsc[C];
-  __shared__ float gpart[PARTS][DK];
+  __shared__ float beta_s[C];
 
   OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oKt);
   OpT* Kh_s = reinterpret_cast<OpT*>(sm + Sm::oKh);
@@ -229,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   float* TT_s = reinterpret_cast<float*>(sm + Sm::oKh);  // T column-major: TT[s][r] = T[r][s]
   float* A_s = reinterpret_cast<float*>(sm + Sm::oKe);   // A row-major
   float* X_s = reinterpret_cast<float*>(sm + Sm::oX);
+  float* gpart = reinterpret_cast<float*>(sm + Sm::oG);  // [PARTS][DK], before P exists
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -248,117 +256,116 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   const size_t qk_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_qk + hq;  // row t0
   const size_t g_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_v + h;
 
-  // ---- 1. this thread's channel column: k, q (and g) for its rows ----
-  const int c = tid % DK;
-  const int part = tid / DK;
-  const int rlo = part * RPP;
-  float kc[RPP], qc[RPP], gc[RPP];
+  // ---- 1. loads: this thread's channel quad over its rows, branch-free ----
+  // (rows past the end load a valid row and are then multiplied by zero, so the
+  // unrolled loads stay in registers)
+  const int c4 = tid % Sm::NQ;
+  const int part = tid / Sm::NQ;
+  const bool active = part < PARTS;
+  const int rlo = active ? part * RPP : 0;
+  float kq[RPP][4], qq[RPP][4], gq[RPP][4];
 #pragma unroll
   for (int i = 0; i < RPP; ++i) {
     const int r = rlo + i;
-    const int rr = r < L ? r : L - 1;  // rows past the end: load a valid row, then zero it
-    const float m = r < L ? 1.0f : 0.0f;
-    const size_t off = (qk_row0 + static_cast<size_t>(rr) * a.H_qk) * DK + c;
-    kc[i] = m * to_f32(kg[off]);
-    qc[i] = m * to_f32(qg[off]);
-    gc[i] = a.gate == GDR_GATE_CHANNEL
-                ? m * a.gate_in[(g_row0 + static_cast<size_t>(rr) * a.H_v) * DK + c]
-                : 0.0f;
+    const int rr = r < L ? r : L - 1;
+    const float m = (active && r < L) ? 1.0f : 0.0f;
+    const size_t off = (qk_row0 + static_cast<size_t>(rr) * a.H_qk) * DK + 4 * c4;
+    load_row<OpT, 4>(kg + off, kq[i]);
+    load_row<OpT, 4>(qg + off, qq[i]);
+    const size_t gi = g_row0 + static_cast<size_t>(rr) * a.H_v;
+    if (a.gate == GDR_GATE_CHANNEL) {
+      load_row<float, 4>(a.gate_in + gi * DK + 4 * c4, gq[i]);
+    } else {
+      const float g1 = a.gate == GDR_GATE_SCALAR
+                           ? a.gate_in[gi]
+                           : fused_log_decay(a.gate_in[gi], a.A_log[h], a.dt_bias[h]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) gq[i][u] = g1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kq[i][u] *= m;
+      qq[i][u] *= m;
+      gq[i][u] *= m;
+    }
+    if (active && c4 == 0) beta_s[r] = r < L ? sigmoidf(a.beta_logit[gi]) : 0.0f;
   }
 
-  // ---- 2. per-row L2 norms, beta, scalar gate (wave w: rows w, w+4, ...) ----
-  {
-    constexpr int RW = C / (kThreads / 64);  // rows per wave
-    constexpr int EPL = DK >= 64 ? DK / 64 : 1;  // elements per lane
-    float sk[RW], sq[RW];
+  // ---- 2. row L2 norms: sum over the part's NQ consecutive lanes ----
+  if (a.l2norm) {
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int r = wave + 4 * i;
-      sk[i] = sq[i] = 0.0f;
-      if (r < L && a.l2norm && lane * EPL < DK) {
-        const size_t off = (qk_row0 + static_cast<size_t>(r) * a.H_qk) * DK + lane * EPL;
+    for (int i = 0; i < RPP; ++i) {
+      float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float x = to_f32(kg[off + e]);
-          const float y = to_f32(qg[off + e]);
-          sk[i] += x * x;
-          sq[i] += y * y;
-        }
+      for (int u = 0; u < 4; ++u) {
+        sk += kq[i][u] * kq[i][u];
+        sq += qq[i][u] * qq[i][u];
+      }
+#pragma unroll
+      for (int off = Sm::NQ / 2; off > 0; off >>= 1) {
+        sk += __shfl_xor(sk, off, 64);
+        sq += __shfl_xor(sq, off, 64);
+      }
+      const float ik = 1.0f / sqrtf(sk + kL2Eps), iq = 1.0f / sqrtf(sq + kL2Eps);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kq[i][u] *= ik;
+        qq[i][u] *= iq;
       }
     }
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      sk[i] = wave_sum(sk[i]);
-      sq[i] = wave_sum(sq[i]);
-    }
-    if (lane < RW) {
-      // lane i publishes row wave + 4 i (select the i-th entry without dynamic indexing)
-      float vk = 0.f, vq = 0.f;
-#pragma unroll
-      for (int i = 0; i < RW; ++i)
-        if (lane == i) {
-          vk = sk[i];
-          vq = sq[i];
-        }
-      const int r = wave + 4 * lane;
-      const bool valid = r < L;
-      inv_nk[r] = a.l2norm ? 1.0f / sqrtf(vk + kL2Eps) : 1.0f;
-      inv_nq[r] = a.l2norm ? 1.0f / sqrtf(vq + kL2Eps) : 1.0f;
-      const size_t gi = g_row0 + static_cast<size_t>(r) * a.H_v;
-      beta_s[r] = valid ? sigmoidf(a.beta_logit[gi]) : 0.0f;
-      float g = 0.0f;
-      if (valid && a.gate == GDR_GATE_SCALAR) g = a.gate_in[gi];
-      if (valid && a.gate == GDR_GATE_SCALAR_FUSED)
-        g = fused_log_decay(a.gate_in[gi], a.A_log[h], a.dt_bias[h]);
-      gsc[r] = g;
-    }
   }
-  __syncthreads();
 
-  // ---- 3. prefix sums and decayed operands ----
-  if (a.gate != GDR_GATE_CHANNEL) {
+  // ---- 3. per-channel prefix sums and decayed operands ----
+  float gam[4] = {0.f, 0.f, 0.f, 0.f}, total[4] = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < RPP; ++i) gc[i] = gsc[rlo + i];
-  }
-  {
-    float s = 0.f;
+    for (int i = 0; i < RPP; ++i)
 #pragma unroll
-    for (int i = 0; i < RPP; ++i) s += gc[i];
-    gpart[part][c] = s;
+      for (int u = 0; u < 4; ++u) sp[u] += gq[i][u];
+    *reinterpret_cast<float4*>(gpart + part * DK + 4 * c4) = make_float4(sp[0], sp[1], sp[2], sp[3]);
   }
   __syncthreads();
-  float gam = 0.f, total = 0.f;
+  if (active) {
+    for (int p = 0; p < PARTS; ++p) {
+      const float4 x = *reinterpret_cast<const float4*>(gpart + p * DK + 4 * c4);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-  for (int p = 0; p < PARTS; ++p) {
-    const float x = gpart[p][c];
-    if (p < part) gam += x;
-    total += x;
-  }
-  // gam: Gamma just before row rlo; total: Gamma_L.
-  constexpr int KG = RPP < 4 ? RPP : 4;  // Ke^T values written per LDS store
-#pragma unroll
-  for (int i0 = 0; i0 < RPP; i0 += KG) {
-    OpT ke[KG];
-#pragma unroll
-    for (int u = 0; u < KG; ++u) {
-      const int i = i0 + u;
-      const int r = rlo + i;
-      gam += gc[i];
-      const float kv = kc[i] * inv_nk[r];
-      const float qv = qc[i] * inv_nq[r];
-      const float e_pos = expf(gam);
-      const float e_neg = expf(-gam);
-      Kt_s[r * LDK + c] = from_f32<OpT>(kv * e_pos);
-      Kh_s[r * LDK + c] = from_f32<OpT>(kv * e_neg);
-      Qt_s[r * LDK + c] = from_f32<OpT>(qv * e_pos);
-      ke[u] = from_f32<OpT>(kv * expf(total - gam));
+      for (int u = 0; u < 4; ++u) {
+        if (p < part) gam[u] += xv[u];
+        total[u] += xv[u];
+      }
     }
-    OpT* dst = KeT_s + c * LDC + rlo + i0;
+    // gam: Gamma just before row rlo; total: Gamma_L, per channel of the quad.
+    OpT ke[4][RPP];
 #pragma unroll
-    for (int u = 0; u < KG; ++u) dst[u] = ke[u];
+    for (int i = 0; i < RPP; ++i) {
+      const int r = rlo + i;
+      OpT kt[4], kh[4], qt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        gam[u] += gq[i][u];
+        const float e_pos = expf(gam[u]);
+        const float e_neg = expf(-gam[u]);
+        kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
+        kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
+        qt[u] = from_f32<OpT>(qq[i][u] * e_pos);
+        ke[u][i] = from_f32<OpT>(kq[i][u] * expf(total[u] - gam[u]));
+      }
+      store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
+      store_vec4<OpT>(Kh_s + r * LDK + 4 * c4, kh);
+      store_vec4<OpT>(Qt_s + r * LDK + 4 * c4, qt);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      OpT* dst = KeT_s + (4 * c4 + u) * LDC + rlo;
+#pragma unroll
+      for (int i = 0; i < RPP; ++i) dst[i] = ke[u][i];
+    }
+    if (part == 0)
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(blk_bytes + Blk::kGammaByte) + 4 * c4) =
+          make_float4(expf(total[0]), expf(total[1]), expf(total[2]), expf(total[3]));
   }
-  if (part == 0)
-    reinterpret_cast<float*>(blk_bytes + Blk::kGammaByte)[c] = expf(total);
   __syncthreads();
 
   // ---- copy Kt, Qt, Ke^T out (16-byte pieces); Ke^T's storage is reused by A ----
@@ -407,6 +414,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   __syncthreads();  // Kh is dead: its storage becomes T (column-major)
 
   // ---- 5a. diagonal 16x16 blocks of (I + A)^-1: lane = column ----
+  // x_r = -sum_{m<r} A_rm x_m, with four independent partial sums per row
+  // and each row of A read as broadcast float4s.
   if (wave < NB && lane < 16) {
     const int o = 16 * wave;
     const int s = lane;
@@ -415,9 +424,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
     for (int r = 0; r < 16; ++r) x[r] = r == s ? 1.0f : 0.0f;
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
-      float acc = 0.0f;
+      const float* arow = A_s + (o + r) * LDT + o;
+      float part_sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < r; ++m) acc += A_s[(o + r) * LDT + o + m] * x[m];
+      for (int m4 = 0; m4 < r; m4 += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(arow + m4);
+        const float aa[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (m4 + u < r) part_sum[u] += aa[u] * x[m4 + u];
+      }
+      const float acc = (part_sum[0] + part_sum[1]) + (part_sum[2] + part_sum[3]);
       if (r > s) x[r] = -acc;
     }
     float* col = TT_s + (o + s) * LDT + o;

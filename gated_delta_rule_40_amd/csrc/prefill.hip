@@ -214,6 +214,12 @@ struct PrepSmem {
   static constexpr size_t kP = static_cast<size_t>(C) * LDC * sizeof(OpT);
   static constexpr size_t kG = static_cast<size_t>(PARTS) * DK * sizeof(float);
   static constexpr size_t oG = oP;
+  // The row-norm partials (phase 2) live where Kt goes later.
+  static constexpr int LDN = 2 * NQ + 1;
+  static constexpr size_t oN = oKt;
+  static_assert(static_cast<size_t>(C) * LDN * sizeof(float) <= kOpRows ||
+                    static_cast<size_t>(C) * LDN * sizeof(float) <= oKh - oKt,
+                "norm partials must fit in Kt's storage");
   static constexpr size_t kBytes = al16(oP + (kP > kG ? kP : kG));
 };
 
@@ -291,26 +297,43 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
     if (active && c4 == 0) beta_s[r] = r < L ? sigmoidf(a.beta_logit[gi]) : 0.0f;
   }
 
-  // ---- 2. row L2 norms: sum over the part's NQ consecutive lanes ----
+  // ---- 2. row L2 norms: each thread leaves its quad's partial sums in LDS,
+  //         one thread per row adds them up ----
+  float* nrm = reinterpret_cast<float*>(sm + Sm::oN);  // [C][2 NQ + 1] partials, then 1/norms
   if (a.l2norm) {
+    if (active) {
 #pragma unroll
-    for (int i = 0; i < RPP; ++i) {
+      for (int i = 0; i < RPP; ++i) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sk += kq[i][u] * kq[i][u];
+          sq += qq[i][u] * qq[i][u];
+        }
+        nrm[(rlo + i) * Sm::LDN + c4] = sk;
+        nrm[(rlo + i) * Sm::LDN + Sm::NQ + c4] = sq;
+      }
+    }
+    __syncthreads();
+    if (tid < C) {
       float sk = 0.f, sq = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sk += kq[i][u] * kq[i][u];
-        sq += qq[i][u] * qq[i][u];
+      for (int q = 0; q < Sm::NQ; ++q) {
+        sk += nrm[tid * Sm::LDN + q];
+        sq += nrm[tid * Sm::LDN + Sm::NQ + q];
       }
+      nrm[tid * Sm::LDN] = 1.0f / sqrtf(sk + kL2Eps);
+      nrm[tid * Sm::LDN + 1] = 1.0f / sqrtf(sq + kL2Eps);
+    }
+    __syncthreads();
+    if (active) {
 #pragma unroll
-      for (int off = Sm::NQ / 2; off > 0; off >>= 1) {
-        sk += __shfl_xor(sk, off, 64);
-        sq += __shfl_xor(sq, off, 64);
-      }
-      const float ik = 1.0f / sqrtf(sk + kL2Eps), iq = 1.0f / sqrtf(sq + kL2Eps);
+      for (int i = 0; i < RPP; ++i) {
+        const float ik = nrm[(rlo + i) * Sm::LDN], iq = nrm[(rlo + i) * Sm::LDN + 1];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        kq[i][u] *= ik;
-        qq[i][u] *= iq;
+        for (int u = 0; u < 4; ++u) {
+          kq[i][u] *= ik;
+          qq[i][u] *= iq;
+        }
       }
     }
   }
@@ -345,12 +368,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         gam[u] += gq[i][u];
-        const float e_pos = expf(gam[u]);
-        const float e_neg = expf(-gam[u]);
+        const float e_pos = __expf(gam[u]);
+        const float e_neg = __expf(-gam[u]);
         kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
         kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
         qt[u] = from_f32<OpT>(qq[i][u] * e_pos);
-        ke[u][i] = from_f32<OpT>(kq[i][u] * expf(total[u] - gam[u]));
+        ke[u][i] = from_f32<OpT>(kq[i][u] * __expf(total[u] - gam[u]));
       }
       store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
       store_vec4<OpT>(Kh_s + r * LDK + 4 * c4, kh);

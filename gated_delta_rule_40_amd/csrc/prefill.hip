@@ -26,10 +26,14 @@
 //   chunk_carry  one workgroup per (b, h, slice of DVS state columns), walking
 //                the chunks in order with its state slice held in MFMA
 //                accumulators; the columns of S are independent, so slices
-//                need no communication.  The next chunk's operands are
-//                prefetched into registers while the current one computes.
+//                need no communication.  Operand fragments go straight from
+//                the workspace into registers: as soon as a phase has used
+//                its fragments, the same registers load that phase's
+//                fragments of the next chunk.
 // Dense products use MFMA (bf16 operands with fp32 accumulation for bf16 io,
 // fp32 MFMA for fp32 io); the triangular solve runs in fp32 in LDS.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gdr_internal.h"
 #include "gdr.h"
@@ -104,51 +108,13 @@ __device__ __forceinline__ void store_tile_t(OpT* Y, int ldy, int y_row0, int y_
 // Rows of the workspace block's operand regions are stored XOR-swizzled in
 // 16-byte pieces: piece p of row r sits at position p ^ swz_key(r, ppr), ppr
 // being the row's piece count.  For any 16 consecutive rows and a fixed p the
-// stored pieces then fall in 16 distinct groups of 4 LDS banks, so the MFMA
-// operand reads (16 rows, one piece each) are conflict-free after a straight
-// copy of the block into LDS.
+// stored pieces then fall in 16 distinct groups of 4 LDS banks, so a straight
+// copy of the block into LDS gives conflict-free MFMA operand reads.  The
+// carry reads the block straight into MFMA fragments instead; there the XOR
+// only permutes the 64-byte groups of a row and the pieces inside them, so
+// each fragment row is still one aligned 64-byte read.
 __host__ __device__ constexpr int swz_key(int r, int ppr) {
   return ppr >= 16 ? (r & 15) : ((r / (16 / ppr)) % ppr);
-}
-
-// acc += X Z^T like mma_xzt, with X read from a swizzled block region whose
-// rows are `ppr` pieces wide; Z is a padded row-major LDS buffer.
-template <typename OpT, int KD>
-__device__ __forceinline__ f32x4 mma_swz(const OpT* __restrict__ X, int ppr, int x0,
-                                         const OpT* __restrict__ Z, int ldz, int z0, f32x4 acc,
-                                         int lane) {
-  constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));
-  const int r = lane & 15;
-  const int kg = lane >> 4;
-  const int key = swz_key(x0 + r, ppr);
-  const OpT* xrow = X + (x0 + r) * ppr * VPER;
-  auto xat = [&](int e) __attribute__((always_inline)) {
-    return xrow + (((e / VPER) ^ key) * VPER) + e % VPER;
-  };
-  if constexpr (sizeof(OpT) == 4) {
-#pragma unroll
-    for (int k = 0; k < KD; k += 4) {
-      float xa = *xat(k + kg);
-      float zb = Z[(z0 + r) * ldz + k + kg];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, zb, acc, 0, 0, 0);
-    }
-  } else if constexpr (KD % 32 == 0) {
-#pragma unroll
-    for (int k = 0; k < KD; k += 32) {
-      bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(xat(k + 8 * kg));
-      bf16x8_t zb = *reinterpret_cast<const bf16x8_t*>(Z + (z0 + r) * ldz + k + 8 * kg);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, zb, acc, 0, 0, 0);
-    }
-  } else {
-    static_assert(KD % 16 == 0, "contraction must be a multiple of 16");
-#pragma unroll
-    for (int k = 0; k < KD; k += 16) {
-      bf16x4_t xa = *reinterpret_cast<const bf16x4_t*>(xat(k + 4 * kg));
-      bf16x4_t zb = *reinterpret_cast<const bf16x4_t*>(Z + (z0 + r) * ldz + k + 4 * kg);
-      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xa, zb, acc, 0, 0, 0);
-    }
-  }
-  return acc;
 }
 
 // Layout of one (b, h, chunk) block of the workspace.
@@ -526,91 +492,169 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
 // chunk_carry
 //
 // One workgroup per (b, h, slice of DVS state columns); the slice of S lives in
-// MFMA accumulators for the whole sequence.  Each chunk's workspace block is
-// brought into LDS by direct-to-LDS loads (global_load_lds_dwordx4), issued
-// one chunk ahead into the other half of a double buffer, so no registers hold
-// the prefetch and the copy overlaps the current chunk's arithmetic.  The
-// block is stored XOR-swizzled (see swz_key), so the straight copy lands in a
-// layout whose MFMA operand reads are free of LDS bank conflicts.
+// MFMA accumulators for the whole sequence.  Every operand the workspace block
+// holds is an A operand of some product, and each wave reads exactly the rows
+// of them its tiles need straight from global memory into registers (the
+// XOR-swizzled block layout is undone in the address), one chunk ahead of
+// their use.  LDS only carries what the waves exchange: S^T, R^T and U^T.
 // Per chunk, three barriers:
-//   [B1]  S^T (operand type) written; this chunk's block has landed
+//   [B1]  S^T (operand type) written
 //   c:    R = V - Kt S (to LDS, transposed), O = Qt S (registers)      [B2]
 //   d:    U = Tb R (to LDS, transposed)                                  [B3]
 //   e:    O += P U -> o;  S = e^Gamma_L . S + Ke^T U
 // ---------------------------------------------------------------------------
-template <typename OpT, int DK, int DVS, int C, int NBUF>
+
+// MFMA fragment of one operand for a contraction of length KD: the 16x16x32
+// bf16 form (8 values per lane) when KD is a multiple of 32, 16x16x16 bf16
+// (4 values) for KD = 16, 16x16x4 fp32 (1 value) for fp32 operands.  Lane l
+// supplies row (l % 16) and k-values step*KS + (l / 16)*VL ... + VL - 1.
+template <typename OpT, int KD>
+struct FragT {
+  static constexpr int KS = sizeof(OpT) == 4 ? 4 : (KD % 32 == 0 ? 32 : 16);
+  static constexpr int VL = KS / 4;
+  static constexpr int STEPS = KD / KS;
+  using T = std::conditional_t<sizeof(OpT) == 4, float,
+                               std::conditional_t<KS == 32, bf16x8_t, bf16x4_t>>;
+  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) {
+    if constexpr (sizeof(OpT) == 4)
+      return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    else if constexpr (KS == 32)
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // A fragment from a swizzled block region whose rows are `ppr` pieces wide.
+  __device__ static __forceinline__ T load_swz(const OpT* region, int ppr, int row0, int step,
+                                               int lane) {
+    constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));
+    const int row = row0 + (lane & 15);
+    const int e = step * KS + (lane >> 4) * VL;
+    const OpT* p = region + row * ppr * VPER + (((e / VPER) ^ swz_key(row, ppr)) * VPER) + e % VPER;
+    return *reinterpret_cast<const T*>(p);
+  }
+  // A fragment from a padded row-major LDS buffer.
+  __device__ static __forceinline__ T load_pad(const OpT* buf, int ld, int row0, int step,
+                                               int lane) {
+    return *reinterpret_cast<const T*>(buf + (row0 + (lane & 15)) * ld + step * KS +
+                                       (lane >> 4) * VL);
+  }
+};
+
+template <typename OpT, int DK, int DVS, int C>
 struct CarryShape {
   using Blk = ChunkBlock<OpT, DK, C>;
+  using FK = FragT<OpT, DK>;  // contraction over key channels
+  using FC = FragT<OpT, C>;   // contraction over the chunk's tokens
   static constexpr int P = pad_of<OpT>();
   static constexpr int LDK = DK + P;  // rows of St
   static constexpr int LDC = C + P;   // rows of Rt, Ut
-  // Eight waves (two per SIMD) once a slice has enough tiles to share out.
-  static constexpr int NT = DVS >= 32 ? 512 : 256;
-  static constexpr int NW = NT / 64;
-  static constexpr int NST = (DK / 16) * (DVS / 16);  // state tiles
+  static constexpr int NW = DVS >= 32 ? 8 : 4;        // waves (two per SIMD from 32 columns)
+  static constexpr int NT = 64 * NW;
+  static constexpr int DVT = DVS / 16;
+  static constexpr int NST = (DK / 16) * DVT;         // state tiles
   static constexpr int SPW = (NST + NW - 1) / NW;      // state tiles per wave
-  static constexpr int NOT = (C / 16) * (DVS / 16);   // output tiles
+  static constexpr int NOT = (C / 16) * DVT;          // output tiles
   static constexpr int OPW = (NOT + NW - 1) / NW;
-  static constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));
-  static constexpr int kPieces = static_cast<int>(Blk::kBytes / 16);  // block, 16-byte pieces
-  static constexpr int kVRowPieces = DVS / VPER;                      // V row of the slice
-  static constexpr int kVPieces = C * kVRowPieces;
-  static constexpr size_t kBuf = Blk::kBytes;
-  static constexpr size_t kVBuf = static_cast<size_t>(C) * DVS * sizeof(OpT);
-  static constexpr size_t kSmem = NBUF * (kBuf + kVBuf) +
-                                  sizeof(OpT) * (DVS * LDK + 2 * DVS * LDC);
+  static constexpr int PPR_K = DK * static_cast<int>(sizeof(OpT)) / 16;  // pieces per row
+  static constexpr int PPR_C = C * static_cast<int>(sizeof(OpT)) / 16;
+  static constexpr size_t kSmem = sizeof(OpT) * (DVS * LDK + 2 * DVS * LDC);
 };
 
-// Direct-to-LDS copy of chunk nn's workspace block and V slice into one
-// buffer of the carry kernel.  Wave w moves 16-byte pieces w*64 + NT j + lane
-// (lanes past the end idle); the hardware writes lane i's piece at LDS
-// base + 16 i, so each wave instruction fills 1 KiB of the buffer in order.
-template <typename OpT, int DK, int DVS, int C, int NBUF>
-__device__ __forceinline__ void carry_issue(const PrefillArgs& a, const unsigned char* ws_head,
-                                            unsigned char* dst, OpT* vdst_e, int nn, int b,
-                                            int h, int jb, int wave, int lane, int part,
-                                            int parts) {
-  using Sh = CarryShape<OpT, DK, DVS, C, NBUF>;
+template <typename OpT, int DK, int DVS, int C>
+struct CarryFrags {
+  using Sh = CarryShape<OpT, DK, DVS, C>;
+  typename Sh::FK::T kt[Sh::OPW][Sh::FK::STEPS], qt[Sh::OPW][Sh::FK::STEPS];
+  typename Sh::FC::T tb[Sh::OPW][Sh::FC::STEPS], p[Sh::OPW][Sh::FC::STEPS];
+  typename Sh::FC::T ke[Sh::SPW][Sh::FC::STEPS];
+  float v[Sh::OPW][4];
+  float gam[Sh::SPW][4];
+};
+
+// Issue the loads of chunk nn's fragments for this wave's tiles, by phase:
+// phase c needs Kt, Qt and V; phase d Tb; phase e P, Ke^T and e^Gamma_L.
+template <typename OpT, int DK, int DVS, int C, int PHASE>
+__device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
+                                           const unsigned char* ws_head, int nn, int b, int h,
+                                           int jb, int wave, int lane) {
+  using Sh = CarryShape<OpT, DK, DVS, C>;
   using Blk = typename Sh::Blk;
-  typedef __attribute__((address_space(3))) void* lds_ptr;
-  // Part `part` of `parts` moves every parts-th 256-piece row of the block, so
-  // the copy can be spread over the phases of the current chunk.
-  const unsigned char* src = ws_head + static_cast<size_t>(nn) * Blk::kBytes;
-  for (int base = wave * 64 + part * Sh::NT; base < Sh::kPieces; base += parts * Sh::NT) {
-    const int piece = base + lane;
-    if (piece < Sh::kPieces)
-      __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(piece) * 16,
-                                       (lds_ptr)(dst + base * 16), 16, 0, 0);
-  }
-  if (part != parts - 1) return;
-  const int t0 = nn * C;
+  using FK = typename Sh::FK;
+  using FC = typename Sh::FC;
+  const unsigned char* blk_bytes = ws_head + static_cast<size_t>(nn) * Blk::kBytes;
+  const OpT* blk = reinterpret_cast<const OpT*>(blk_bytes);
   const OpT* vg = static_cast<const OpT*>(a.v);
-  unsigned char* vdst = reinterpret_cast<unsigned char*>(vdst_e);
-  for (int base = wave * 64; base < Sh::kVPieces; base += Sh::NT) {
-    const int piece = base + lane;
-    if (piece < Sh::kVPieces) {
-      const int r = piece / Sh::kVRowPieces;
-      const int col = (piece % Sh::kVRowPieces) * Sh::VPER;
-      const int t = min(t0 + r, a.T - 1);  // rows past the end are masked when read
-      const OpT* p = vg + ((static_cast<size_t>(b) * a.T + t) * a.H_v + h) * a.dv + jb + col;
-      __builtin_amdgcn_global_load_lds(p, (lds_ptr)(vdst + base * 16), 16, 0, 0);
+  const int t0 = nn * C;
+#pragma unroll
+  for (int i = 0; i < Sh::OPW; ++i) {
+    const int t = wave * Sh::OPW + i;
+    if (Sh::NOT % Sh::NW == 0 || t < Sh::NOT) {
+      const int R = t / Sh::DVT, J = t % Sh::DVT;
+      if constexpr (PHASE == 0) {
+#pragma unroll
+        for (int s = 0; s < FK::STEPS; ++s) {
+          F.kt[i][s] = FK::load_swz(blk + Blk::kKt, Sh::PPR_K, 16 * R, s, lane);
+          F.qt[i][s] = FK::load_swz(blk + Blk::kQt, Sh::PPR_K, 16 * R, s, lane);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + 4 * (lane >> 4) + e;
+          const int tt = min(t0 + r, a.T - 1);  // rows past the end are zeroed when used
+          F.v[i][e] = to_f32(vg[((static_cast<size_t>(b) * a.T + tt) * a.H_v + h) * a.dv + jb +
+                                16 * J + (lane & 15)]);
+        }
+      }
+      if constexpr (PHASE == 1) {
+#pragma unroll
+        for (int s = 0; s < FC::STEPS; ++s)
+          F.tb[i][s] = FC::load_swz(blk + Blk::kTb, Sh::PPR_C, 16 * R, s, lane);
+      }
+      if constexpr (PHASE == 2) {
+#pragma unroll
+        for (int s = 0; s < FC::STEPS; ++s)
+          F.p[i][s] = FC::load_swz(blk + Blk::kP, Sh::PPR_C, 16 * R, s, lane);
+      }
+    }
+  }
+  if constexpr (PHASE == 2) {
+    const float* gam = reinterpret_cast<const float*>(blk_bytes + Blk::kGammaByte);
+#pragma unroll
+    for (int j = 0; j < Sh::SPW; ++j) {
+      const int t = wave * Sh::SPW + j;
+      if (Sh::NST % Sh::NW == 0 || t < Sh::NST) {
+        const int I = t / Sh::DVT;
+#pragma unroll
+        for (int s = 0; s < FC::STEPS; ++s)
+          F.ke[j][s] = FC::load_swz(blk + Blk::kKeT, Sh::PPR_C, 16 * I, s, lane);
+        const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
+        F.gam[j][0] = g4.x;
+        F.gam[j][1] = g4.y;
+        F.gam[j][2] = g4.z;
+        F.gam[j][3] = g4.w;
+      }
     }
   }
 }
 
-template <typename OpT, int DK, int DVS, int C, int NBUF>
-__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, NBUF>::NT)) void chunk_carry_kernel(
-    PrefillArgs a) {
-  using Sh = CarryShape<OpT, DK, DVS, C, NBUF>;
-  using Blk = typename Sh::Blk;
-  constexpr int LDK = Sh::LDK, LDC = Sh::LDC;
-  constexpr int SPW = Sh::SPW, OPW = Sh::OPW, NST = Sh::NST, NOT = Sh::NOT;
-  constexpr int DVT = DVS / 16;
-  constexpr int PPR_K = DK * static_cast<int>(sizeof(OpT)) / 16;  // pieces per row, [.][DK]
-  constexpr int PPR_C = C * static_cast<int>(sizeof(OpT)) / 16;   // pieces per row, [.][C]
+template <typename OpT, int DK, int DVS, int C>
+__device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C>& F,
+                                               const PrefillArgs& a, const unsigned char* ws_head,
+                                               int nn, int b, int h, int jb, int wave, int lane) {
+  carry_load<OpT, DK, DVS, C, 0>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, 1>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, 2>(F, a, ws_head, nn, b, h, jb, wave, lane);
+}
 
-  __shared__ __attribute__((aligned(16))) unsigned char bufs[NBUF][Sh::kBuf];
-  __shared__ __attribute__((aligned(16))) OpT vbufs[NBUF][C * DVS];
+template <typename OpT, int DK, int DVS, int C>
+__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry_kernel(
+    PrefillArgs a) {
+  using Sh = CarryShape<OpT, DK, DVS, C>;
+  using Blk = typename Sh::Blk;
+  using FK = typename Sh::FK;
+  using FC = typename Sh::FC;
+  using Frags = CarryFrags<OpT, DK, DVS, C>;
+  constexpr int LDK = Sh::LDK, LDC = Sh::LDC, DVT = Sh::DVT;
+  constexpr int SPW = Sh::SPW, OPW = Sh::OPW, NST = Sh::NST, NOT = Sh::NOT;
+
   __shared__ __attribute__((aligned(16))) OpT St_s[DVS * LDK];
   __shared__ __attribute__((aligned(16))) OpT Rt_s[DVS * LDC];
   __shared__ __attribute__((aligned(16))) OpT Ut_s[DVS * LDC];
@@ -644,7 +688,7 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, NBUF>::NT)) void chunk
   for (int i = 0; i < SPW; ++i) {
     const int t = wave * SPW + i;
     sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < NST && a.state_in) {
+    if ((NST % Sh::NW == 0 || t < NST) && a.state_in) {
       const int I = t / DVT, J = t % DVT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -655,59 +699,26 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, NBUF>::NT)) void chunk
     }
   }
 
-  // The outputs of chunk nn are stored at the start of chunk nn+1, right after
-  // its wait for the block copies: vmcnt also counts stores, so storing them
-  // earlier would make that wait sit out their write acknowledgements.
-  f32x4 opend[OPW];
-  int t0_pend = 0, L_pend = 0;
-  auto store_pending = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < OPW; ++i) {
-      const int t = wave * OPW + i;
-      if (t < NOT) {
-        const int R = t / DVT, J = t % DVT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * R + 4 * (lane >> 4) + e;
-          if (r < L_pend)
-            og[((static_cast<size_t>(b) * a.T + t0_pend + r) * a.H_v + h) * a.dv + jb + 16 * J +
-               (lane & 15)] = from_f32<OpT>(a.scale * opend[i][e]);
-        }
-      }
-    }
-  };
-
-  carry_issue<OpT, DK, DVS, C, NBUF>(a, ws_head, bufs[0], vbufs[0], 0, b, h, jb, wave, lane, 0,
-                                     1);
-  for (int nn = 0; nn < NC; ++nn) {
+  // One register set of fragments: as soon as a phase has consumed its
+  // fragments, the same registers start loading that phase's fragments of the
+  // next chunk, so each load has most of a chunk step to arrive.
+  auto compute = [&](Frags& F, int nn) __attribute__((always_inline)) {
     const int t0 = nn * C;
     const int L = min(C, a.T - t0);
-    const int cur = NBUF == 2 ? (nn & 1) : 0;
-    const OpT* Kt_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kKt;
-    const OpT* Qt_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kQt;
-    const OpT* KeT_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kKeT;
-    const OpT* Tb_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kTb;
-    const OpT* P_b = reinterpret_cast<const OpT*>(bufs[cur]) + Blk::kP;
-    const float* gam_b = reinterpret_cast<const float*>(bufs[cur] + Blk::kGammaByte);
-    const OpT* V_b = vbufs[cur];
-
+    // The last chunk reloads itself (in bounds, unused) so that every load is
+    // unconditional and the wait counters stay exact across iterations.
+    const int nx = min(nn + 1, NC - 1);
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = wave * SPW + i;
-      if (t < NST) {
+      if (NST % Sh::NW == 0 || t < NST) {
         const int I = t / DVT, J = t % DVT;
         float v[4] = {sacc[i][0], sacc[i][1], sacc[i][2], sacc[i][3]};
         store_tile_t<OpT>(St_s, LDK, 16 * J, 16 * I, v, lane);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of chunk nn landed
-    __syncthreads();                                     // [B1] ... and everyone else's
-    // The next chunk's copy overlaps this chunk's arithmetic.
-    if (NBUF == 2 && nn + 1 < NC)
-      carry_issue<OpT, DK, DVS, C, NBUF>(a, ws_head, bufs[cur ^ 1], vbufs[cur ^ 1], nn + 1, b, h,
-                                         jb, wave, lane, 0, 1);
-    if (nn > 0) store_pending();
+    __syncthreads();  // [B1]
 
     // R = V - Kt S  (stored transposed),  O = Qt S (kept in registers).
     f32x4 oacc[OPW];
@@ -715,73 +726,92 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, NBUF>::NT)) void chunk
     for (int i = 0; i < OPW; ++i) {
       const int t = wave * OPW + i;
       oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < NOT) {
+      if (NOT % Sh::NW == 0 || t < NOT) {
         const int R = t / DVT, J = t % DVT;
         f32x4 ks = {0.f, 0.f, 0.f, 0.f};
-        ks = mma_swz<OpT, DK>(Kt_b, PPR_K, 16 * R, St_s, LDK, 16 * J, ks, lane);
-        oacc[i] = mma_swz<OpT, DK>(Qt_b, PPR_K, 16 * R, St_s, LDK, 16 * J, oacc[i], lane);
+#pragma unroll
+        for (int s = 0; s < FK::STEPS; ++s) {
+          const auto z = FK::load_pad(St_s, LDK, 16 * J, s, lane);
+          ks = FK::mma(F.kt[i][s], z, ks);
+          oacc[i] = FK::mma(F.qt[i][s], z, oacc[i]);
+        }
         float rv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * R + 4 * (lane >> 4) + e;
-          const float vv = r < L ? to_f32(V_b[r * DVS + 16 * J + (lane & 15)]) : 0.0f;
-          rv[e] = vv - ks[e];
+          rv[e] = (r < L ? F.v[i][e] : 0.0f) - ks[e];
         }
         store_tile_t<OpT>(Rt_s, LDC, 16 * J, 16 * R, rv, lane);
       }
     }
+    carry_load<OpT, DK, DVS, C, 0>(F, a, ws_head, nx, b, h, jb, wave, lane);
     __syncthreads();  // [B2]
 
     // U = Tb R  (stored transposed).
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
       const int t = wave * OPW + i;
-      if (t < NOT) {
+      if (NOT % Sh::NW == 0 || t < NOT) {
         const int R = t / DVT, J = t % DVT;
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
-        u = mma_swz<OpT, C>(Tb_b, PPR_C, 16 * R, Rt_s, LDC, 16 * J, u, lane);
+#pragma unroll
+        for (int s = 0; s < FC::STEPS; ++s)
+          u = FC::mma(F.tb[i][s], FC::load_pad(Rt_s, LDC, 16 * J, s, lane), u);
         float uv[4] = {u[0], u[1], u[2], u[3]};
         store_tile_t<OpT>(Ut_s, LDC, 16 * J, 16 * R, uv, lane);
       }
     }
+    carry_load<OpT, DK, DVS, C, 1>(F, a, ws_head, nx, b, h, jb, wave, lane);
     __syncthreads();  // [B3]
 
-    // O = Qt S + P U, stored (times scale) at the start of the next chunk.
+    // O = scale (Qt S + P U) -> o rows of this chunk.
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
       const int t = wave * OPW + i;
-      if (t < NOT) {
+      if (NOT % Sh::NW == 0 || t < NOT) {
         const int R = t / DVT, J = t % DVT;
-        opend[i] = mma_swz<OpT, C>(P_b, PPR_C, 16 * R, Ut_s, LDC, 16 * J, oacc[i], lane);
+#pragma unroll
+        for (int s = 0; s < FC::STEPS; ++s)
+          oacc[i] = FC::mma(F.p[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), oacc[i]);
+        OpT* orow = og + ((static_cast<size_t>(b) * a.T + t0 + 16 * R + 4 * (lane >> 4)) * a.H_v +
+                          h) * a.dv + jb + 16 * J + (lane & 15);
+        const size_t rstride = static_cast<size_t>(a.H_v) * a.dv;
+        if (L == C) {  // full chunk: no per-row guard
+#pragma unroll
+          for (int e = 0; e < 4; ++e) orow[e * rstride] = from_f32<OpT>(a.scale * oacc[i][e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * R + 4 * (lane >> 4) + e < L)
+              orow[e * rstride] = from_f32<OpT>(a.scale * oacc[i][e]);
+        }
       }
     }
-    t0_pend = t0;
-    L_pend = L;
     // S = diag(e^Gamma_L) S + Ke^T U.
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = wave * SPW + i;
-      if (t < NST) {
-        const int I = t / DVT, J = t % DVT;
+      if (NST % Sh::NW == 0 || t < NST) {
+        const int J = t % DVT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[i][e] *= gam_b[16 * I + 4 * (lane >> 4) + e];
-        sacc[i] = mma_swz<OpT, C>(KeT_b, PPR_C, 16 * I, Ut_s, LDC, 16 * J, sacc[i], lane);
+        for (int e = 0; e < 4; ++e) sacc[i][e] *= F.gam[i][e];
+#pragma unroll
+        for (int s = 0; s < FC::STEPS; ++s)
+          sacc[i] = FC::mma(F.ke[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), sacc[i]);
       }
     }
-    if (NBUF == 1 && nn + 1 < NC) {
-      __syncthreads();  // single buffer: everyone is done with it before it is refilled
-      carry_issue<OpT, DK, DVS, C, NBUF>(a, ws_head, bufs[0], vbufs[0], nn + 1, b, h, jb, wave,
-                                         lane, 0, 1);
-    }
-  }
+    carry_load<OpT, DK, DVS, C, 2>(F, a, ws_head, nx, b, h, jb, wave, lane);
+  };
 
-  if (NC > 0) store_pending();
+  Frags F;
+  carry_load_all<OpT, DK, DVS, C>(F, a, ws_head, 0, b, h, jb, wave, lane);
+  for (int nn = 0; nn < NC; ++nn) compute(F, nn);
 
   // ---- final state ----
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     const int t = wave * SPW + i;
-    if (t < NST) {
+    if (NST % Sh::NW == 0 || t < NST) {
       const int I = t / DVT, J = t % DVT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -821,48 +851,26 @@ size_t block_bytes_rt(int dk, int chunk) {
   return 0;
 }
 
-constexpr size_t kSmemLimit = 160 * 1024;
-
-template <typename OpT, int DK, int DVS, int C, int NBUF>
-constexpr bool carry_fits() {
-  return CarryShape<OpT, DK, DVS, C, NBUF>::kSmem <= kSmemLimit;
-}
-
-template <typename OpT, int DK, int DVS, int C, int NBUF>
-hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (!carry_fits<OpT, DK, DVS, C, NBUF>()) {
-    return hipErrorInvalidConfiguration;
-  } else {
-    const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
-    hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, NBUF>), dim3(grid),
-                       dim3(CarryShape<OpT, DK, DVS, C, NBUF>::NT),
-                       0, stream, a);
-    return hipGetLastError();
-  }
-}
-
-// Slice width: the narrowest (from 32 columns, 8 waves) that keeps the
-// (b, h, slice) workgroups within one per CU, since each takes most of a CU's
-// LDS; the chunk block is double-buffered when that fits in LDS.
 template <typename OpT, int DK, int DVS, int C>
-hipError_t launch_carry_buf(const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (carry_fits<OpT, DK, DVS, C, 2>())
-    return launch_carry<OpT, DK, DVS, C, 2>(a, stream);
-  else
-    return launch_carry<OpT, DK, DVS, C, 1>(a, stream);
+hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
+  hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C>), dim3(grid),
+                     dim3(CarryShape<OpT, DK, DVS, C>::NT), 0, stream, a);
+  return hipGetLastError();
 }
 
+// Slice width: the narrowest from 32 columns (8 waves) that keeps the number
+// of (b, h, slice) workgroups within two per CU, and at most 64 columns (wider
+// slices would not fit their fragments in registers).
 template <typename OpT, int DK, int C>
 hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
   const long units = static_cast<long>(a.B) * a.H_v;
   int dvs = a.dv < 32 ? a.dv : 32;
-  while (dvs < a.dv && units * (a.dv / dvs) > 256) dvs *= 2;
-  if (dvs > a.dv) dvs = a.dv;
+  while (dvs < a.dv && dvs < 64 && units * (a.dv / dvs) > 512) dvs *= 2;
   switch (dvs) {
-    case 16: return launch_carry_buf<OpT, DK, 16, C>(a, stream);
-    case 32: return launch_carry_buf<OpT, DK, 32, C>(a, stream);
-    case 64: return launch_carry_buf<OpT, DK, 64, C>(a, stream);
-    default: return launch_carry_buf<OpT, DK, 128, C>(a, stream);
+    case 16: return launch_carry<OpT, DK, 16, C>(a, stream);
+    case 32: return launch_carry<OpT, DK, 32, C>(a, stream);
+    default: return launch_carry<OpT, DK, 64, C>(a, stream);
   }
 }
 

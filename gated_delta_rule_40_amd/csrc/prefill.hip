@@ -105,19 +105,51 @@ __device__ __forceinline__ void store_tile_t(OpT* Y, int ldy, int y_row0, int y_
   }
 }
 
-// Rows of the workspace block's operand regions are stored XOR-swizzled in
-// 16-byte pieces: piece p of row r sits at position p ^ swz_key(r, ppr), ppr
-// being the row's piece count.  For any 16 consecutive rows and a fixed p the
-// stored pieces then fall in 16 distinct groups of 4 LDS banks, so a straight
-// copy of the block into LDS gives conflict-free MFMA operand reads.  The
-// carry reads the block straight into MFMA fragments instead; there the XOR
-// only permutes the 64-byte groups of a row and the pieces inside them, so
-// each fragment row is still one aligned 64-byte read.
-__host__ __device__ constexpr int swz_key(int r, int ppr) {
-  return ppr >= 16 ? (r & 15) : ((r / (16 / ppr)) % ppr);
-}
+// MFMA fragment of one operand for a contraction of length KD: the 16x16x32
+// bf16 form (8 values per lane) when KD is a multiple of 32, 16x16x16 bf16
+// (4 values) for KD = 16, 16x16x4 fp32 (1 value) for fp32 operands.  Lane l
+// supplies row (l % 16) and k-values step*KS + (l / 16)*VL ... + VL - 1.
+template <typename OpT, int KD>
+struct FragT {
+  static constexpr int KS = sizeof(OpT) == 4 ? 4 : (KD % 32 == 0 ? 32 : 16);
+  static constexpr int VL = KS / 4;
+  static constexpr int STEPS = KD / KS;
+  using T = std::conditional_t<sizeof(OpT) == 4, float,
+                               std::conditional_t<KS == 32, bf16x8_t, bf16x4_t>>;
+  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) {
+    if constexpr (sizeof(OpT) == 4)
+      return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    else if constexpr (KS == 32)
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // Workspace blocks hold every operand region in fragment order: for each
+  // 16-row tile and contraction step, the 64 lanes' VL-element slices back
+  // to back, so a fragment is one contiguous read of 64 * VL elements.
+  // Slot d (VL elements) holds row slot_row(d) at columns slot_col(d) ...
+  // slot_col(d) + VL - 1 of the region.
+  __host__ __device__ static constexpr int slot_row(int d) {
+    return 16 * (d / (64 * STEPS)) + d % 16;
+  }
+  __host__ __device__ static constexpr int slot_col(int d) {
+    return ((d / 64) % STEPS) * KS + ((d / 16) % 4) * VL;
+  }
+  // The fragment of rows row0 ... row0 + 15 (row0 a multiple of 16), `step`.
+  __device__ static __forceinline__ T load(const OpT* region, int row0, int step, int lane) {
+    return *reinterpret_cast<const T*>(region + ((row0 / 16 * STEPS + step) * 64 + lane) * VL);
+  }
+  // A fragment from a padded row-major LDS buffer.
+  __device__ static __forceinline__ T load_pad(const OpT* buf, int ld, int row0, int step,
+                                               int lane) {
+    return *reinterpret_cast<const T*>(buf + (row0 + (lane & 15)) * ld + step * KS +
+                                       (lane >> 4) * VL);
+  }
+};
 
-// Layout of one (b, h, chunk) block of the workspace.
+// Layout of one (b, h, chunk) block of the workspace.  The operand regions are
+// in fragment order (FragT::slot_row / slot_col): Kt and Qt for a
+// contraction over DK, the others over C.
 template <typename OpT, int DK, int C>
 struct ChunkBlock {
   static constexpr int kKt = 0;                  // [C][DK]  K e^Gamma
@@ -195,7 +227,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   using Blk = ChunkBlock<OpT, DK, C>;
   constexpr int LDK = Sm::LDK, LDC = Sm::LDC, LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
   constexpr int PARTS = Sm::PARTS, RPP = Sm::RPP;
-  constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));  // elements per 16-byte piece
 
   __shared__ __attribute__((aligned(16))) unsigned char sm[Sm::kBytes];
   __shared__ float beta_s[C];
@@ -357,21 +388,24 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   }
   __syncthreads();
 
-  // ---- copy Kt, Qt, Ke^T out (16-byte pieces); Ke^T's storage is reused by A ----
+  // ---- copy Kt, Qt, Ke^T out in fragment order; Ke^T's storage is reused by A ----
   {
-    constexpr int PR = DK / VPER;  // pieces per row of Kt / Qt
-    constexpr int PC = C / VPER;   // pieces per row of Ke^T
-    uint4* out = reinterpret_cast<uint4*>(blk_bytes);
-    for (int p = tid; p < C * PR; p += kThreads) {
-      const int r = p / PR, q = p % PR;
-      const int qs = q ^ swz_key(r, PR);
-      out[(Blk::kKt + r * DK) / VPER + qs] = *reinterpret_cast<const uint4*>(Kt_s + r * LDK + q * VPER);
-      out[(Blk::kQt + r * DK) / VPER + qs] = *reinterpret_cast<const uint4*>(Qt_s + r * LDK + q * VPER);
+    using FK = FragT<OpT, DK>;
+    using FC = FragT<OpT, C>;
+    using SK = typename FK::T;
+    using SC = typename FC::T;
+    OpT* out = reinterpret_cast<OpT*>(blk_bytes);
+    for (int d = tid; d < C * DK / FK::VL; d += kThreads) {
+      const int r = FK::slot_row(d), c = FK::slot_col(d);
+      *reinterpret_cast<SK*>(out + Blk::kKt + d * FK::VL) =
+          *reinterpret_cast<const SK*>(Kt_s + r * LDK + c);
+      *reinterpret_cast<SK*>(out + Blk::kQt + d * FK::VL) =
+          *reinterpret_cast<const SK*>(Qt_s + r * LDK + c);
     }
-    for (int p = tid; p < DK * PC; p += kThreads) {
-      const int r = p / PC, q = p % PC;
-      out[(Blk::kKeT + r * C) / VPER + (q ^ swz_key(r, PC))] =
-          *reinterpret_cast<const uint4*>(KeT_s + r * LDC + q * VPER);
+    for (int d = tid; d < DK * C / FC::VL; d += kThreads) {
+      const int r = FC::slot_row(d), c = FC::slot_col(d);
+      *reinterpret_cast<SC*>(out + Blk::kKeT + d * FC::VL) =
+          *reinterpret_cast<const SC*>(KeT_s + r * LDC + c);
     }
   }
   __syncthreads();
@@ -469,21 +503,23 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // ---- 6. Tb = T diag(beta) and P out, 16-byte pieces ----
+  // ---- 6. Tb = T diag(beta) and P out, in fragment order ----
   {
-    constexpr int PC = C / VPER;
-    uint4* out = reinterpret_cast<uint4*>(blk_bytes);
-    for (int p = tid; p < C * PC; p += kThreads) {
-      const int r = p / PC, s0 = (p % PC) * VPER;
-      OpT v[VPER];
+    using FC = FragT<OpT, C>;
+    using SC = typename FC::T;
+    constexpr int VL = FC::VL;
+    OpT* out = reinterpret_cast<OpT*>(blk_bytes);
+    for (int d = tid; d < C * C / VL; d += kThreads) {
+      const int r = FC::slot_row(d), c = FC::slot_col(d);
+      OpT v[VL];
 #pragma unroll
-      for (int u = 0; u < VPER; ++u) {
-        const int s = s0 + u;
+      for (int u = 0; u < VL; ++u) {
+        const int s = c + u;
         v[u] = from_f32<OpT>(r >= s ? TT_s[s * LDT + r] * beta_s[s] : 0.0f);
       }
-      const int qs = (p % PC) ^ swz_key(r, PC);
-      out[(Blk::kTb + r * C) / VPER + qs] = *reinterpret_cast<const uint4*>(v);
-      out[(Blk::kP + r * C) / VPER + qs] = *reinterpret_cast<const uint4*>(P_s + r * LDC + s0);
+      *reinterpret_cast<SC*>(out + Blk::kTb + d * VL) = *reinterpret_cast<const SC*>(v);
+      *reinterpret_cast<SC*>(out + Blk::kP + d * VL) =
+          *reinterpret_cast<const SC*>(P_s + r * LDC + c);
     }
   }
 }
@@ -494,8 +530,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
 // One workgroup per (b, h, slice of DVS state columns); the slice of S lives in
 // MFMA accumulators for the whole sequence.  Every operand the workspace block
 // holds is an A operand of some product, and each wave reads exactly the rows
-// of them its tiles need straight from global memory into registers (the
-// XOR-swizzled block layout is undone in the address), one chunk ahead of
+// of them its tiles need straight from global memory into registers (each
+// fragment one contiguous read, the block being in fragment order), ahead of
 // their use.  LDS only carries what the waves exchange: S^T, R^T and U^T.
 // Per chunk, three barriers:
 //   [B1]  S^T (operand type) written
@@ -504,41 +540,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
 //   e:    O += P U -> o;  S = e^Gamma_L . S + Ke^T U
 // ---------------------------------------------------------------------------
 
-// MFMA fragment of one operand for a contraction of length KD: the 16x16x32
-// bf16 form (8 values per lane) when KD is a multiple of 32, 16x16x16 bf16
-// (4 values) for KD = 16, 16x16x4 fp32 (1 value) for fp32 operands.  Lane l
-// supplies row (l % 16) and k-values step*KS + (l / 16)*VL ... + VL - 1.
-template <typename OpT, int KD>
-struct FragT {
-  static constexpr int KS = sizeof(OpT) == 4 ? 4 : (KD % 32 == 0 ? 32 : 16);
-  static constexpr int VL = KS / 4;
-  static constexpr int STEPS = KD / KS;
-  using T = std::conditional_t<sizeof(OpT) == 4, float,
-                               std::conditional_t<KS == 32, bf16x8_t, bf16x4_t>>;
-  __device__ static __forceinline__ f32x4 mma(T a, T b, f32x4 c) {
-    if constexpr (sizeof(OpT) == 4)
-      return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-    else if constexpr (KS == 32)
-      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    else
-      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-  }
-  // A fragment from a swizzled block region whose rows are `ppr` pieces wide.
-  __device__ static __forceinline__ T load_swz(const OpT* region, int ppr, int row0, int step,
-                                               int lane) {
-    constexpr int VPER = 16 / static_cast<int>(sizeof(OpT));
-    const int row = row0 + (lane & 15);
-    const int e = step * KS + (lane >> 4) * VL;
-    const OpT* p = region + row * ppr * VPER + (((e / VPER) ^ swz_key(row, ppr)) * VPER) + e % VPER;
-    return *reinterpret_cast<const T*>(p);
-  }
-  // A fragment from a padded row-major LDS buffer.
-  __device__ static __forceinline__ T load_pad(const OpT* buf, int ld, int row0, int step,
-                                               int lane) {
-    return *reinterpret_cast<const T*>(buf + (row0 + (lane & 15)) * ld + step * KS +
-                                       (lane >> 4) * VL);
-  }
-};
 
 template <typename OpT, int DK, int DVS, int C>
 struct CarryShape {
@@ -555,8 +556,6 @@ struct CarryShape {
   static constexpr int SPW = (NST + NW - 1) / NW;      // state tiles per wave
   static constexpr int NOT = (C / 16) * DVT;          // output tiles
   static constexpr int OPW = (NOT + NW - 1) / NW;
-  static constexpr int PPR_K = DK * static_cast<int>(sizeof(OpT)) / 16;  // pieces per row
-  static constexpr int PPR_C = C * static_cast<int>(sizeof(OpT)) / 16;
   static constexpr size_t kSmem = sizeof(OpT) * (DVS * LDK + 2 * DVS * LDC);
 };
 
@@ -592,26 +591,29 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
       if constexpr (PHASE == 0) {
 #pragma unroll
         for (int s = 0; s < FK::STEPS; ++s) {
-          F.kt[i][s] = FK::load_swz(blk + Blk::kKt, Sh::PPR_K, 16 * R, s, lane);
-          F.qt[i][s] = FK::load_swz(blk + Blk::kQt, Sh::PPR_K, 16 * R, s, lane);
+          F.kt[i][s] = FK::load(blk + Blk::kKt, 16 * R, s, lane);
+          F.qt[i][s] = FK::load(blk + Blk::kQt, 16 * R, s, lane);
         }
+        // Uniform row base plus 32-bit lane offsets; rows past the end re-read
+        // the last row and are zeroed when used.
+        const OpT* vrow = vg + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
+        const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
+        const int last = a.T - 1 - t0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * R + 4 * (lane >> 4) + e;
-          const int tt = min(t0 + r, a.T - 1);  // rows past the end are zeroed when used
-          F.v[i][e] = to_f32(vg[((static_cast<size_t>(b) * a.T + tt) * a.H_v + h) * a.dv + jb +
-                                16 * J + (lane & 15)]);
+          const int r = min(16 * R + 4 * (lane >> 4) + e, last);
+          F.v[i][e] = to_f32(vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)]);
         }
       }
       if constexpr (PHASE == 1) {
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s)
-          F.tb[i][s] = FC::load_swz(blk + Blk::kTb, Sh::PPR_C, 16 * R, s, lane);
+          F.tb[i][s] = FC::load(blk + Blk::kTb, 16 * R, s, lane);
       }
       if constexpr (PHASE == 2) {
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s)
-          F.p[i][s] = FC::load_swz(blk + Blk::kP, Sh::PPR_C, 16 * R, s, lane);
+          F.p[i][s] = FC::load(blk + Blk::kP, 16 * R, s, lane);
       }
     }
   }
@@ -624,7 +626,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
         const int I = t / Sh::DVT;
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s)
-          F.ke[j][s] = FC::load_swz(blk + Blk::kKeT, Sh::PPR_C, 16 * I, s, lane);
+          F.ke[j][s] = FC::load(blk + Blk::kKeT, 16 * I, s, lane);
         const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
         F.gam[j][0] = g4.x;
         F.gam[j][1] = g4.y;
@@ -700,13 +702,13 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   }
 
   // One register set of fragments: as soon as a phase has consumed its
-  // fragments, the same registers start loading that phase's fragments of the
-  // next chunk, so each load has most of a chunk step to arrive.
+  // fragments, the same registers start loading that phase's fragments of
+  // the next chunk, so each load has most of a chunk step to arrive.  The
+  // last chunk re-reads itself (in bounds, unused), keeping every load
+  // unconditional so that the wait counters stay exact across iterations.
   auto compute = [&](Frags& F, int nn) __attribute__((always_inline)) {
     const int t0 = nn * C;
     const int L = min(C, a.T - t0);
-    // The last chunk reloads itself (in bounds, unused) so that every load is
-    // unconditional and the wait counters stay exact across iterations.
     const int nx = min(nn + 1, NC - 1);
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll
@@ -773,17 +775,19 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s)
           oacc[i] = FC::mma(F.p[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), oacc[i]);
-        OpT* orow = og + ((static_cast<size_t>(b) * a.T + t0 + 16 * R + 4 * (lane >> 4)) * a.H_v +
-                          h) * a.dv + jb + 16 * J + (lane & 15);
-        const size_t rstride = static_cast<size_t>(a.H_v) * a.dv;
+        OpT* obase = og + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
+        const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
+        const unsigned r0 = 16 * R + 4 * (lane >> 4);
+        const unsigned col = 16 * J + (lane & 15);
         if (L == C) {  // full chunk: no per-row guard
 #pragma unroll
-          for (int e = 0; e < 4; ++e) orow[e * rstride] = from_f32<OpT>(a.scale * oacc[i][e]);
+          for (int e = 0; e < 4; ++e)
+            obase[(r0 + e) * rs + col] = from_f32<OpT>(a.scale * oacc[i][e]);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (16 * R + 4 * (lane >> 4) + e < L)
-              orow[e * rstride] = from_f32<OpT>(a.scale * oacc[i][e]);
+            if (static_cast<int>(r0) + e < L)
+              obase[(r0 + e) * rs + col] = from_f32<OpT>(a.scale * oacc[i][e]);
         }
       }
     }

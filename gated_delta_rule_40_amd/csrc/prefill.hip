@@ -863,14 +863,17 @@ hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Slice width: the narrowest from 32 columns (8 waves) that keeps the number
-// of (b, h, slice) workgroups within two per CU, and at most 64 columns (wider
-// slices would not fit their fragments in registers).
+// Slice width: the narrowest (from 16 columns) that keeps the number of
+// (b, h, slice) workgroups within one per CU, and at most 64 columns (wider
+// slices would not fit their fragments in registers).  A chunk step of a
+// workgroup costs more the wider its slice, but a second workgroup on a CU
+// costs more still: the carry is a chain of dependent steps, so two chains
+// sharing a CU's load path and matrix cores each run slower.
 template <typename OpT, int DK, int C>
 hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
   const long units = static_cast<long>(a.B) * a.H_v;
-  int dvs = a.dv < 32 ? a.dv : 32;
-  while (dvs < a.dv && dvs < 64 && units * (a.dv / dvs) > 512) dvs *= 2;
+  int dvs = a.dv < 16 ? a.dv : 16;
+  while (dvs < a.dv && dvs < 64 && units * (a.dv / dvs) > 256) dvs *= 2;
   switch (dvs) {
     case 16: return launch_carry<OpT, DK, 16, C>(a, stream);
     case 32: return launch_carry<OpT, DK, 32, C>(a, stream);

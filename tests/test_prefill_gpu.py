@@ -79,6 +79,23 @@ def test_prefill_head_dims(dk, dv, io):
     assert rel(o, o_ref) < TOL[io] and rel(S, S_ref) < TOL[io]
 
 
+@pytest.mark.parametrize("B", [1, 2, 4])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_slice_widths(B, io):
+    """H 16 -> 32, dk=dv=128 at B=1, 2, 4: the carry splits dv into slices of
+    16, 32 and 64 columns respectively (one workgroup per CU), so every slice
+    width and its fragment schedule is checked against the oracle, with a
+    nonzero initial state and a ragged last chunk."""
+    require_gpu()
+    case = synth.prefill_case("slices", 300 + B, B, 150, 16, 32, 128, 128, 64, io,
+                              synth.GATE_CHANNEL, 0.001, 0.2, 0.02)
+    announce(f"prefill slices io={io} B={B} T=150 H 16->32 dk=dv=128 chunk=64")
+    o, S = run_prefill(case)
+    o_ref, S_ref = _oracle(case)
+    print(f"err o={rel(o, o_ref):.3e} S={rel(S, S_ref):.3e}")
+    assert rel(o, o_ref) < TOL[io] and rel(S, S_ref) < TOL[io]
+
+
 @pytest.mark.timeout(600)
 def test_prefill_t4000_bf16_channel():
     """B=1, T=4000 (62 full chunks of 64 and one of 32), H 16 -> 32, dk=dv=128."""

@@ -221,7 +221,9 @@ struct PrepSmem {
   static constexpr size_t kBytes = al16(oP + (kP > kG ? kP : kG));
 };
 
-template <typename OpT, int DK, int C>
+// kChannel: per-channel log-decays (one per key channel and row); otherwise one
+// per row (plain or fused), broadcast over the channels.
+template <typename OpT, int DK, int C, bool kChannel>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   using Sm = PrepSmem<OpT, DK, C>;
   using Blk = ChunkBlock<OpT, DK, C>;
@@ -259,39 +261,58 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   const size_t qk_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_qk + hq;  // row t0
   const size_t g_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_v + h;
 
-  // ---- 1. loads: this thread's channel quad over its rows, branch-free ----
-  // (rows past the end load a valid row and are then multiplied by zero, so the
-  // unrolled loads stay in registers)
+  // ---- 1. loads: this thread's channel quad over its rows ----
+  // Every load of the phase is issued before any value is used: the row
+  // loops hold no branch (the gate kind is decided around them) and beta is
+  // read by one thread per row afterwards, so all loads are in flight at
+  // once.  Rows past the end load a valid row and are then multiplied by zero.
+  static_assert(C <= kThreads, "one thread per row reads beta");
   const int c4 = tid % Sm::NQ;
   const int part = tid / Sm::NQ;
   const bool active = part < PARTS;
   const int rlo = active ? part * RPP : 0;
   float kq[RPP][4], qq[RPP][4], gq[RPP][4];
+  // beta first: its wait then covers no other load
+  const float beta_x =
+      tid < C ? a.beta_logit[g_row0 + static_cast<size_t>(min(tid, L - 1)) * a.H_v] : 0.0f;
 #pragma unroll
   for (int i = 0; i < RPP; ++i) {
-    const int r = rlo + i;
-    const int rr = r < L ? r : L - 1;
-    const float m = (active && r < L) ? 1.0f : 0.0f;
+    const int rr = min(rlo + i, L - 1);
     const size_t off = (qk_row0 + static_cast<size_t>(rr) * a.H_qk) * DK + 4 * c4;
     load_row<OpT, 4>(kg + off, kq[i]);
     load_row<OpT, 4>(qg + off, qq[i]);
-    const size_t gi = g_row0 + static_cast<size_t>(rr) * a.H_v;
-    if (a.gate == GDR_GATE_CHANNEL) {
-      load_row<float, 4>(a.gate_in + gi * DK + 4 * c4, gq[i]);
-    } else {
-      const float g1 = a.gate == GDR_GATE_SCALAR
-                           ? a.gate_in[gi]
-                           : fused_log_decay(a.gate_in[gi], a.A_log[h], a.dt_bias[h]);
+  }
+  if constexpr (kChannel) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) gq[i][u] = g1;
+    for (int i = 0; i < RPP; ++i) {
+      const size_t gi = g_row0 + static_cast<size_t>(min(rlo + i, L - 1)) * a.H_v;
+      load_row<float, 4>(a.gate_in + gi * DK + 4 * c4, gq[i]);
     }
+  } else {
+    float g1[RPP];
+#pragma unroll
+    for (int i = 0; i < RPP; ++i)
+      g1[i] = a.gate_in[g_row0 + static_cast<size_t>(min(rlo + i, L - 1)) * a.H_v];
+    if (a.gate == GDR_GATE_SCALAR_FUSED) {
+      const float A_log = a.A_log[h], dt_bias = a.dt_bias[h];
+#pragma unroll
+      for (int i = 0; i < RPP; ++i) g1[i] = fused_log_decay(g1[i], A_log, dt_bias);
+    }
+#pragma unroll
+    for (int i = 0; i < RPP; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) gq[i][u] = g1[i];
+  }
+  if (tid < C) beta_s[tid] = tid < L ? sigmoidf(beta_x) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < RPP; ++i) {
+    const float m = (active && rlo + i < L) ? 1.0f : 0.0f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       kq[i][u] *= m;
       qq[i][u] *= m;
       gq[i][u] *= m;
     }
-    if (active && c4 == 0) beta_s[r] = r < L ? sigmoidf(a.beta_logit[gi]) : 0.0f;
   }
 
   // ---- 2. row L2 norms: each thread leaves its quad's partial sums in LDS,
@@ -885,8 +906,12 @@ template <typename OpT, int DK, int C>
 hipError_t launch_dk_c(const PrefillArgs& a, hipStream_t stream) {
   const int NC = (a.T + C - 1) / C;
   const unsigned prep_grid = static_cast<unsigned>(a.B) * a.H_v * NC;
-  hipLaunchKernelGGL((chunk_prep_kernel<OpT, DK, C>), dim3(prep_grid), dim3(kThreads), 0, stream,
-                     a);
+  if (a.gate == GDR_GATE_CHANNEL)
+    hipLaunchKernelGGL((chunk_prep_kernel<OpT, DK, C, true>), dim3(prep_grid), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<OpT, DK, C, false>), dim3(prep_grid), dim3(kThreads), 0,
+                       stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_carry_any<OpT, DK, C>(a, stream);

@@ -166,16 +166,20 @@ struct ChunkBlock {
 // chunk_prep
 //
 // Per (b, h, chunk):
-//   1. every global load of the chunk is issued up front (rows of q and k for
-//      the L2 norms; per-thread channel columns of k, q, g for the decays);
-//   2. row norms, beta and the scalar gate per row;
+//   1. every global load of the chunk is issued up front (per-thread channel
+//      quads of k, q, g over a part of the rows; beta once per row);
+//   2. row norms through LDS partial sums;
 //   3. per-channel prefix sums (each channel split into row parts, combined
 //      through LDS) and the decayed operands, built in fp32 and rounded once;
-//   4. A and P on MFMA;
+//      Kt, Qt and Ke^T leave for the block from registers;
+//   4. A and P on MFMA, computed transposed so that each lane holds four
+//      consecutive columns of a row; P leaves for the block from registers;
 //   5. (I + A)^-1 blocked by 16: the diagonal 16x16 blocks by forward
 //      substitution in registers (one lane per column), then the off-diagonal
 //      blocks level by level, T_ij = -T_ii sum_k A_ik T_kj, with fp32 MFMA;
-//   6. everything leaves through LDS in 16-byte coalesced stores.
+//   6. Tb = T diag(beta) leaves for the block in coalesced lane slices.
+// LDS holds three regions that are reused phase by phase (PrepSmem), small
+// enough for three workgroups per CU at dk = 128, C = 64, bf16.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -184,7 +188,6 @@ __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
 template <typename OpT, int DK, int C>
 struct PrepSmem {
   static constexpr int LDK = DK + pad_of<OpT>();  // rows of Kt, Kh, Qt
-  static constexpr int LDC = C + pad_of<OpT>();   // rows of Ke^T and P
   static constexpr int LDT = C + 4;               // fp32 A (row-major), T (column-major)
   static constexpr int LDX = 20;                  // fp32 16x16 scratch of the solve
   static constexpr int NB = C / 16;
@@ -195,31 +198,53 @@ struct PrepSmem {
   static constexpr int NTA = PARTS * NQ;                               // active threads
   static constexpr int RPP = C / PARTS;                                // rows per part
   static_assert(NTA <= kThreads && NTA % 64 == 0 && C % PARTS == 0, "prep split");
+  static_assert(NB <= kThreads / 64, "one wave per diagonal block of the solve");
+  static constexpr int LDN = 2 * NQ + 1;  // row-norm partials: [C][2 NQ + 1]
+  static constexpr size_t al16(size_t x) { return (x + 15) / 16 * 16; }
+  static constexpr size_t mx(size_t x, size_t y) { return x > y ? x : y; }
   static constexpr size_t kOpRows = static_cast<size_t>(C) * LDK * sizeof(OpT);
   static constexpr size_t kTm = static_cast<size_t>(C) * LDT * sizeof(float);
-  static constexpr size_t kKeT = static_cast<size_t>(DK) * LDC * sizeof(OpT);
-  static constexpr size_t al16(size_t x) { return (x + 15) / 16 * 16; }
   static constexpr size_t kX = 4 * 16 * LDX * sizeof(float);
-  // Byte offsets.  Once A and P are done, Kh's storage holds T (column-major)
-  // and Qt's the solve scratch; Ke^T's holds A once Ke^T has been copied out.
-  static constexpr size_t oKt = 0;
-  static constexpr size_t oKh = al16(oKt + kOpRows);
-  static constexpr size_t oQt = al16(oKh + (kOpRows > kTm ? kOpRows : kTm));
-  static constexpr size_t oKe = al16(oQt + (kOpRows > kX ? kOpRows : kX));
-  static constexpr size_t oP = al16(oKe + (kKeT > kTm ? kKeT : kTm));
-  static constexpr size_t oX = oQt;
-  // The per-part channel sums of the prefix phase live where P goes later.
-  static constexpr size_t kP = static_cast<size_t>(C) * LDC * sizeof(OpT);
+  static constexpr size_t kN = static_cast<size_t>(C) * LDN * sizeof(float);
   static constexpr size_t kG = static_cast<size_t>(PARTS) * DK * sizeof(float);
-  static constexpr size_t oG = oP;
-  // The row-norm partials (phase 2) live where Kt goes later.
-  static constexpr int LDN = 2 * NQ + 1;
-  static constexpr size_t oN = oKt;
-  static_assert(static_cast<size_t>(C) * LDN * sizeof(float) <= kOpRows ||
-                    static_cast<size_t>(C) * LDN * sizeof(float) <= oKh - oKt,
-                "norm partials must fit in Kt's storage");
-  static constexpr size_t kBytes = al16(oP + (kP > kG ? kP : kG));
+  // Three regions, each reused as the chunk moves on (a barrier between uses):
+  //   R0: row-norm partials -> Kt -> Qt (once A is done) -> solve scratch
+  //   R1: Kh -> T, column-major (once P is done)
+  //   R2: per-part channel sums of the prefix -> A
+  static constexpr size_t oR0 = 0;
+  static constexpr size_t oR1 = al16(mx(mx(kOpRows, kN), kX));
+  static constexpr size_t oR2 = oR1 + al16(mx(kOpRows, kTm));
+  static constexpr size_t kBytes = oR2 + al16(mx(kTm, kG));
 };
+
+// Element offset of (row, col) in a region held in fragment order.
+template <typename OpT, int KD>
+__device__ __forceinline__ int frag_off(int row, int col) {
+  using F = FragT<OpT, KD>;
+  return (((row / 16 * F::STEPS + col / F::KS) * 4 + (col % F::KS) / F::VL) * 16 + row % 16) *
+             F::VL +
+         col % F::VL;
+}
+
+// Store N consecutive values of one row, columns col0 ... col0 + N - 1 (col0 a
+// multiple of N), into a region held in fragment order: runs of up to one
+// lane slice are contiguous there and go out as single vector stores.
+template <typename OpT, int KD, int N>
+__device__ __forceinline__ void frag_store(OpT* region, int row, int col0, const OpT (&v)[N]) {
+  constexpr int VL = FragT<OpT, KD>::VL;
+  constexpr int G = N < VL ? N : VL;
+  constexpr int kB = G * static_cast<int>(sizeof(OpT));
+  static_assert(kB == 2 || kB == 4 || kB == 8 || kB == 16, "store width");
+  using W = std::conditional_t<
+      kB == 2, unsigned short,
+      std::conditional_t<kB == 4, unsigned, std::conditional_t<kB == 8, uint2, uint4>>>;
+#pragma unroll
+  for (int j = 0; j < N / G; ++j) {
+    W w;
+    __builtin_memcpy(&w, &v[j * G], kB);
+    *reinterpret_cast<W*>(region + frag_off<OpT, KD>(row, col0 + j * G)) = w;
+  }
+}
 
 // kChannel: per-channel log-decays (one per key channel and row); otherwise one
 // per row (plain or fused), broadcast over the channels.
@@ -227,21 +252,19 @@ template <typename OpT, int DK, int C, bool kChannel>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   using Sm = PrepSmem<OpT, DK, C>;
   using Blk = ChunkBlock<OpT, DK, C>;
-  constexpr int LDK = Sm::LDK, LDC = Sm::LDC, LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
+  constexpr int LDK = Sm::LDK, LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
   constexpr int PARTS = Sm::PARTS, RPP = Sm::RPP;
 
   __shared__ __attribute__((aligned(16))) unsigned char sm[Sm::kBytes];
   __shared__ float beta_s[C];
 
-  OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oKt);
-  OpT* Kh_s = reinterpret_cast<OpT*>(sm + Sm::oKh);
-  OpT* Qt_s = reinterpret_cast<OpT*>(sm + Sm::oQt);
-  OpT* KeT_s = reinterpret_cast<OpT*>(sm + Sm::oKe);
-  OpT* P_s = reinterpret_cast<OpT*>(sm + Sm::oP);
-  float* TT_s = reinterpret_cast<float*>(sm + Sm::oKh);  // T column-major: TT[s][r] = T[r][s]
-  float* A_s = reinterpret_cast<float*>(sm + Sm::oKe);   // A row-major
-  float* X_s = reinterpret_cast<float*>(sm + Sm::oX);
-  float* gpart = reinterpret_cast<float*>(sm + Sm::oG);  // [PARTS][DK], before P exists
+  OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);
+  OpT* Qt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);     // after A
+  float* X_s = reinterpret_cast<float*>(sm + Sm::oR0);  // after P
+  OpT* Kh_s = reinterpret_cast<OpT*>(sm + Sm::oR1);
+  float* TT_s = reinterpret_cast<float*>(sm + Sm::oR1);  // T column-major: TT[s][r] = T[r][s]
+  float* gpart = reinterpret_cast<float*>(sm + Sm::oR2); // [PARTS][DK]
+  float* A_s = reinterpret_cast<float*>(sm + Sm::oR2);   // A row-major
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -317,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
 
   // ---- 2. row L2 norms: each thread leaves its quad's partial sums in LDS,
   //         one thread per row adds them up ----
-  float* nrm = reinterpret_cast<float*>(sm + Sm::oN);  // [C][2 NQ + 1] partials, then 1/norms
+  float* nrm = reinterpret_cast<float*>(sm + Sm::oR0);  // [C][2 NQ + 1] partials, then 1/norms
   if (a.l2norm) {
     if (active) {
 #pragma unroll
@@ -357,6 +380,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   }
 
   // ---- 3. per-channel prefix sums and decayed operands ----
+  // Kt and Kh go to LDS for A and P.  Kt, Qt and Ke^T also go from registers
+  // straight to the block in fragment order; Qt stays in registers until
+  // Kt's storage is free.
+  OpT* out = reinterpret_cast<OpT*>(blk_bytes);
+  OpT qtr[RPP][4];
   float gam[4] = {0.f, 0.f, 0.f, 0.f}, total[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     float sp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -382,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < RPP; ++i) {
       const int r = rlo + i;
-      OpT kt[4], kh[4], qt[4];
+      OpT kt[4], kh[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         gam[u] += gq[i][u];
@@ -390,72 +418,61 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
         const float e_neg = __expf(-gam[u]);
         kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
         kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
-        qt[u] = from_f32<OpT>(qq[i][u] * e_pos);
+        qtr[i][u] = from_f32<OpT>(qq[i][u] * e_pos);
         ke[u][i] = from_f32<OpT>(kq[i][u] * __expf(total[u] - gam[u]));
       }
       store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
       store_vec4<OpT>(Kh_s + r * LDK + 4 * c4, kh);
-      store_vec4<OpT>(Qt_s + r * LDK + 4 * c4, qt);
+      frag_store<OpT, DK, 4>(out + Blk::kKt, r, 4 * c4, kt);
+      frag_store<OpT, DK, 4>(out + Blk::kQt, r, 4 * c4, qtr[i]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      OpT* dst = KeT_s + (4 * c4 + u) * LDC + rlo;
-#pragma unroll
-      for (int i = 0; i < RPP; ++i) dst[i] = ke[u][i];
-    }
+    for (int u = 0; u < 4; ++u) frag_store<OpT, C, RPP>(out + Blk::kKeT, 4 * c4 + u, rlo, ke[u]);
     if (part == 0)
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(blk_bytes + Blk::kGammaByte) + 4 * c4) =
           make_float4(expf(total[0]), expf(total[1]), expf(total[2]), expf(total[3]));
   }
   __syncthreads();
 
-  // ---- copy Kt, Qt, Ke^T out in fragment order; Ke^T's storage is reused by A ----
-  {
-    using FK = FragT<OpT, DK>;
-    using FC = FragT<OpT, C>;
-    using SK = typename FK::T;
-    using SC = typename FC::T;
-    OpT* out = reinterpret_cast<OpT*>(blk_bytes);
-    for (int d = tid; d < C * DK / FK::VL; d += kThreads) {
-      const int r = FK::slot_row(d), c = FK::slot_col(d);
-      *reinterpret_cast<SK*>(out + Blk::kKt + d * FK::VL) =
-          *reinterpret_cast<const SK*>(Kt_s + r * LDK + c);
-      *reinterpret_cast<SK*>(out + Blk::kQt + d * FK::VL) =
-          *reinterpret_cast<const SK*>(Qt_s + r * LDK + c);
-    }
-    for (int d = tid; d < DK * C / FC::VL; d += kThreads) {
-      const int r = FC::slot_row(d), c = FC::slot_col(d);
-      *reinterpret_cast<SC*>(out + Blk::kKeT + d * FC::VL) =
-          *reinterpret_cast<const SC*>(KeT_s + r * LDC + c);
-    }
+  // ---- 4a. A = strict_lower(diag(beta) Kt Kh^T), one lower 16x16 tile per
+  //          job, computed transposed (Kh Kt^T): each lane then holds four
+  //          consecutive columns of one row of A, one 16-byte LDS store ----
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // jobs are wave-uniform
+  constexpr int NL = NB * (NB + 1) / 2;
+  for (int job = wv; job < NL; job += kThreads / 64) {
+    int R = 0;
+    while ((R + 1) * (R + 2) / 2 <= job) ++R;
+    const int S = job - R * (R + 1) / 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mma_xzt<OpT, DK>(Kh_s, LDK, 16 * S, Kt_s, LDK, 16 * R, acc, lane);
+    const int row = 16 * R + (lane & 15);
+    const int col = 16 * S + 4 * (lane >> 4);
+    const float br = beta_s[row];
+    *reinterpret_cast<float4*>(A_s + row * LDT + col) =
+        make_float4(row > col ? br * acc[0] : 0.0f, row > col + 1 ? br * acc[1] : 0.0f,
+                    row > col + 2 ? br * acc[2] : 0.0f, row > col + 3 ? br * acc[3] : 0.0f);
+  }
+  __syncthreads();  // Kt is dead: its storage takes Qt
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) store_vec4<OpT>(Qt_s + (rlo + i) * LDK + 4 * c4, qtr[i]);
   }
   __syncthreads();
 
-  // ---- 4. A = strict_lower(diag(beta) Kt Kh^T) and P = lower(Qt Kh^T) ----
-  constexpr int NL = NB * (NB + 1) / 2;  // lower-triangular 16x16 tiles
-  for (int job = wave; job < 2 * NL; job += kThreads / 64) {
-    const int tl = job % NL;
-    int R = 0;
-    while ((R + 1) * (R + 2) / 2 <= tl) ++R;
-    const int S = tl - R * (R + 1) / 2;
-    const bool isP = job >= NL;
+  // ---- 4b. P = lower(Qt Kh^T), transposed like A, straight to the block in
+  //          fragment order; tiles above the diagonal are written as zeros ----
+  for (int job = wv; job < NB * NB; job += kThreads / 64) {
+    const int R = job / NB, S = job % NB;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mma_xzt<OpT, DK>(isP ? Qt_s : Kt_s, LDK, 16 * R, Kh_s, LDK, 16 * S, acc, lane);
-    const int col = 16 * S + (lane & 15);
+    if (S <= R) acc = mma_xzt<OpT, DK>(Kh_s, LDK, 16 * S, Qt_s, LDK, 16 * R, acc, lane);
+    const int row = 16 * R + (lane & 15);
+    const int col = 16 * S + 4 * (lane >> 4);
+    OpT v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * R + 4 * (lane >> 4) + e;
-      if (isP)
-        P_s[row * LDC + col] = from_f32<OpT>(row >= col ? acc[e] : 0.0f);
-      else
-        A_s[row * LDT + col] = row > col ? beta_s[row] * acc[e] : 0.0f;
-    }
+    for (int e = 0; e < 4; ++e) v[e] = from_f32<OpT>(row >= col + e ? acc[e] : 0.0f);
+    frag_store<OpT, C, 4>(out + Blk::kP, row, col, v);
   }
-  for (int idx = tid; idx < C * C; idx += kThreads) {  // upper tiles of P are zero
-    const int row = idx / C, col = idx % C;
-    if ((row >> 4) < (col >> 4)) P_s[row * LDC + col] = from_f32<OpT>(0.0f);
-  }
-  __syncthreads();  // Kh is dead: its storage becomes T (column-major)
+  __syncthreads();  // Kh and Qt are dead: their storage takes T and the solve scratch
 
   // ---- 5a. diagonal 16x16 blocks of (I + A)^-1: lane = column ----
   // x_r = -sum_{m<r} A_rm x_m, with four independent partial sums per row
@@ -524,12 +541,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // ---- 6. Tb = T diag(beta) and P out, in fragment order ----
+  // ---- 6. Tb = T diag(beta) out, in fragment order ----
   {
     using FC = FragT<OpT, C>;
     using SC = typename FC::T;
     constexpr int VL = FC::VL;
-    OpT* out = reinterpret_cast<OpT*>(blk_bytes);
     for (int d = tid; d < C * C / VL; d += kThreads) {
       const int r = FC::slot_row(d), c = FC::slot_col(d);
       OpT v[VL];
@@ -539,8 +555,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
         v[u] = from_f32<OpT>(r >= s ? TT_s[s * LDT + r] * beta_s[s] : 0.0f);
       }
       *reinterpret_cast<SC*>(out + Blk::kTb + d * VL) = *reinterpret_cast<const SC*>(v);
-      *reinterpret_cast<SC*>(out + Blk::kP + d * VL) =
-          *reinterpret_cast<const SC*>(P_s + r * LDC + c);
     }
   }
 }

@@ -270,17 +270,27 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int NC = (a.T + C - 1) / C;
-  const int n = blockIdx.x % NC;
-  const int bh = blockIdx.x / NC;
-  const int h = bh % a.H_v;
-  const int b = bh / a.H_v;
-  const int hq = h / (a.H_v / a.H_qk);
+  // Work order: the rep = H_v / H_qk value heads that share a qk head, for one
+  // chunk, are consecutive units, and consecutive units run on one XCD
+  // (workgroups w, w + 8, ... share an XCD), so all but the first read that
+  // chunk's q and k rows from the XCD's L2.
+  const int G = gridDim.x;
+  int unit = blockIdx.x;
+  if (G % 8 == 0) unit = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int rep = a.H_v / a.H_qk;
+  const int r_in = unit % rep;
+  const int n = (unit / rep) % NC;
+  const int bq = unit / (rep * NC);  // b * H_qk + hq
+  const int hq = bq % a.H_qk;
+  const int b = bq / a.H_qk;
+  const int h = hq * rep + r_in;
+  const int bh = b * a.H_v + h;
   const int t0 = n * C;
   const int L = min(C, a.T - t0);
   const OpT* qg = static_cast<const OpT*>(a.q);
   const OpT* kg = static_cast<const OpT*>(a.k);
   unsigned char* blk_bytes =
-      static_cast<unsigned char*>(a.ws) + static_cast<size_t>(blockIdx.x) * Blk::kBytes;
+      static_cast<unsigned char*>(a.ws) + (static_cast<size_t>(bh) * NC + n) * Blk::kBytes;
   const size_t qk_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_qk + hq;  // row t0
   const size_t g_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_v + h;
 

@@ -682,6 +682,39 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
   }
 }
 
+// V rows of output tile (R, J) of chunk nn, in accumulator layout.
+template <typename OpT, int DK, int DVS, int C>
+__device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
+                                             int nn, int b, int h, int jb, int i, int R, int J,
+                                             int lane) {
+  // Uniform row base plus 32-bit lane offsets; rows past the end re-read the
+  // last row and are zeroed when used.
+  const int t0 = nn * C;
+  const OpT* vrow = static_cast<const OpT*>(a.v) +
+                    ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
+  const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
+  const int last = a.T - 1 - t0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = min(16 * R + 4 * (lane >> 4) + e, last);
+    F.v[i][e] = to_f32(vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)]);
+  }
+}
+
+// e^Gamma_L for the rows of state tile row-block I of the block at blk.
+template <typename OpT, int DK, int DVS, int C>
+__device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C>& F, const OpT* blk,
+                                               int i, int I, int lane) {
+  using Blk = typename CarryShape<OpT, DK, DVS, C>::Blk;
+  const float* gam =
+      reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(blk) + Blk::kGammaByte);
+  const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
+  F.gam[i][0] = g4.x;
+  F.gam[i][1] = g4.y;
+  F.gam[i][2] = g4.z;
+  F.gam[i][3] = g4.w;
+}
+
 template <typename OpT, int DK, int DVS, int C>
 __device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C>& F,
                                                const PrefillArgs& a, const unsigned char* ws_head,
@@ -751,10 +784,15 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   // the next chunk, so each load has most of a chunk step to arrive.  The
   // last chunk re-reads itself (in bounds, unused), keeping every load
   // unconditional so that the wait counters stay exact across iterations.
-  auto compute = [&](Frags& F, int nn) __attribute__((always_inline)) {
+  // kFull: the chunk has all C rows (every chunk but a ragged last one), so
+  // the o stores need no row guard and the loop body holds no branch around
+  // memory operations, which keeps the compiler's wait counts exact.
+  auto compute = [&](Frags& F, int nn, auto full) __attribute__((always_inline)) {
+    constexpr bool kFull = decltype(full)::value;
     const int t0 = nn * C;
-    const int L = min(C, a.T - t0);
+    const int L = kFull ? C : min(C, a.T - t0);
     const int nx = min(nn + 1, NC - 1);
+    const OpT* nblk = reinterpret_cast<const OpT*>(ws_head + static_cast<size_t>(nx) * Blk::kBytes);
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -776,11 +814,18 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
       if (NOT % Sh::NW == 0 || t < NOT) {
         const int R = t / DVT, J = t % DVT;
         f32x4 ks = {0.f, 0.f, 0.f, 0.f};
+        typename FK::T z[FK::STEPS];
+        z[0] = FK::load_pad(St_s, LDK, 16 * J, 0, lane);
 #pragma unroll
         for (int s = 0; s < FK::STEPS; ++s) {
-          const auto z = FK::load_pad(St_s, LDK, 16 * J, s, lane);
-          ks = FK::mma(F.kt[i][s], z, ks);
-          oacc[i] = FK::mma(F.qt[i][s], z, oacc[i]);
+          if (s + 1 < FK::STEPS) z[s + 1] = FK::load_pad(St_s, LDK, 16 * J, s + 1, lane);
+          ks = FK::mma(F.kt[i][s], z[s], ks);
+          oacc[i] = FK::mma(F.qt[i][s], z[s], oacc[i]);
+          // The next chunk's fragments go out one pair per step, so the CU's
+          // load path is fed steadily instead of in a burst that stalls issue.
+          F.kt[i][s] = FK::load(nblk + Blk::kKt, 16 * R, s, lane);
+          F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
+          __builtin_amdgcn_sched_barrier(0);
         }
         float rv[4];
 #pragma unroll
@@ -789,9 +834,9 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
           rv[e] = (r < L ? F.v[i][e] : 0.0f) - ks[e];
         }
         store_tile_t<OpT>(Rt_s, LDC, 16 * J, 16 * R, rv, lane);
+        carry_load_v<OpT, DK, DVS, C>(F, a, nx, b, h, jb, i, R, J, lane);
       }
     }
-    carry_load<OpT, DK, DVS, C, 0>(F, a, ws_head, nx, b, h, jb, wave, lane);
     __syncthreads();  // [B2]
 
     // U = Tb R  (stored transposed).
@@ -802,13 +847,15 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
         const int R = t / DVT, J = t % DVT;
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < FC::STEPS; ++s)
+        for (int s = 0; s < FC::STEPS; ++s) {
           u = FC::mma(F.tb[i][s], FC::load_pad(Rt_s, LDC, 16 * J, s, lane), u);
+          F.tb[i][s] = FC::load(nblk + Blk::kTb, 16 * R, s, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         float uv[4] = {u[0], u[1], u[2], u[3]};
         store_tile_t<OpT>(Ut_s, LDC, 16 * J, 16 * R, uv, lane);
       }
     }
-    carry_load<OpT, DK, DVS, C, 1>(F, a, ws_head, nx, b, h, jb, wave, lane);
     __syncthreads();  // [B3]
 
     // O = scale (Qt S + P U) -> o rows of this chunk.
@@ -818,13 +865,16 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
       if (NOT % Sh::NW == 0 || t < NOT) {
         const int R = t / DVT, J = t % DVT;
 #pragma unroll
-        for (int s = 0; s < FC::STEPS; ++s)
+        for (int s = 0; s < FC::STEPS; ++s) {
           oacc[i] = FC::mma(F.p[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), oacc[i]);
+          F.p[i][s] = FC::load(nblk + Blk::kP, 16 * R, s, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         OpT* obase = og + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
         const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
         const unsigned r0 = 16 * R + 4 * (lane >> 4);
         const unsigned col = 16 * J + (lane & 15);
-        if (L == C) {  // full chunk: no per-row guard
+        if constexpr (kFull) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             obase[(r0 + e) * rs + col] = from_f32<OpT>(a.scale * oacc[i][e]);
@@ -841,20 +891,25 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
     for (int i = 0; i < SPW; ++i) {
       const int t = wave * SPW + i;
       if (NST % Sh::NW == 0 || t < NST) {
-        const int J = t % DVT;
+        const int I = t / DVT, J = t % DVT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[i][e] *= F.gam[i][e];
+        carry_load_gam<OpT, DK, DVS, C>(F, nblk, i, I, lane);
 #pragma unroll
-        for (int s = 0; s < FC::STEPS; ++s)
+        for (int s = 0; s < FC::STEPS; ++s) {
           sacc[i] = FC::mma(F.ke[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), sacc[i]);
+          F.ke[i][s] = FC::load(nblk + Blk::kKeT, 16 * I, s, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    carry_load<OpT, DK, DVS, C, 2>(F, a, ws_head, nx, b, h, jb, wave, lane);
   };
 
   Frags F;
   carry_load_all<OpT, DK, DVS, C>(F, a, ws_head, 0, b, h, jb, wave, lane);
-  for (int nn = 0; nn < NC; ++nn) compute(F, nn);
+  const int NF = a.T / C;  // full chunks
+  for (int nn = 0; nn < NF; ++nn) compute(F, nn, std::true_type{});
+  if (NF < NC) compute(F, NF, std::false_type{});
 
   // ---- final state ----
 #pragma unroll

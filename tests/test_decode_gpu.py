@@ -56,6 +56,27 @@ def test_decode_tiny_fp32_33_steps(gate):
     assert eo < TOL["f32"] and es < TOL["f32"]
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_without_l2norm(io):
+    """l2norm_qk = 0: q and k are used as given.  They are pre-scaled by
+    1/sqrt(dk) so that |k| ~ 1 and the recurrence stays bounded."""
+    case = synth.decode_case("nol2", 24, 3, 20, 2, 4, 32, 64, io, synth.GATE_CHANNEL,
+                             0.01, 0.5, 0.3)
+    nqk = 2 * case.H_qk * case.dk
+
+    def mutate(qkv, g, bl):
+        qkv = qkv.copy()
+        qkv[:, :nqk] *= np.float32(1.0 / np.sqrt(case.dk))
+        if io == "bf16":  # the values the kernel sees
+            qkv = synth.bf16_to_f32(synth.f32_to_bf16(qkv))
+        return qkv, g, bl
+
+    announce(f"decode no-l2norm io={io} B=3 H 2->4 dk=32 dv=64 steps=20")
+    eo, es = _decode_run(case, 20, l2norm=False, mutate=mutate)
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[io] and es < TOL[io]
+
+
 def test_decode_tiny_fp32_nonzero_state_scale():
     case = synth.tiny_decode(seed=21, gate=synth.GATE_CHANNEL, s0_std=0.5)
     announce("decode tiny fp32 nonzero S0, scale 0.25")

@@ -96,6 +96,24 @@ def test_prefill_slice_widths(B, io):
     assert rel(o, o_ref) < TOL[io] and rel(S, S_ref) < TOL[io]
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_without_l2norm(io):
+    """l2norm_qk = 0: q and k are used as given, pre-scaled by 1/sqrt(dk) so
+    that |k| ~ 1; ragged against chunk 32, nonzero initial state."""
+    require_gpu()
+    case = synth.prefill_case("nol2", 81, 2, 150, 2, 4, 64, 64, 32, io, synth.GATE_CHANNEL,
+                              0.01, 0.3, 0.3)
+    t = case.tensors
+    for name in ("q", "k"):
+        x = case.values(name) * np.float32(1.0 / np.sqrt(case.dk))
+        t[name] = synth.f32_to_bf16(x) if io == "bf16" else x.astype(np.float32)
+    announce(f"prefill no-l2norm io={io} B=2 T=150 H 2->4 dk=dv=64 chunk=32")
+    o, S = run_prefill(case, l2norm=False)
+    o_ref, S_ref = _oracle(case, l2norm=False)
+    print(f"err o={rel(o, o_ref):.3e} S={rel(S, S_ref):.3e}")
+    assert rel(o, o_ref) < TOL[io] and rel(S, S_ref) < TOL[io]
+
+
 @pytest.mark.timeout(600)
 def test_prefill_t4000_bf16_channel():
     """B=1, T=4000 (62 full chunks of 64 and one of 32), H 16 -> 32, dk=dv=128."""

@@ -39,7 +39,8 @@ struct DecodeShape {
   static_assert(DK % RG == 0, "rows must split evenly");
 };
 
-template <typename IoT, int DK, int DVS>
+// kChannel: per-channel log-decays; otherwise one per (b, h), plain or fused.
+template <typename IoT, int DK, int DVS, bool kChannel>
 __global__ __launch_bounds__((DecodeShape<DK, DVS>::NT)) void decode_kernel(DecodeArgs a) {
   using Sh = DecodeShape<DK, DVS>;
   constexpr int C4 = Sh::C4, RPT = Sh::RPT, NW = Sh::NW;
@@ -60,56 +61,74 @@ __global__ __launch_bounds__((DecodeShape<DK, DVS>::NT)) void decode_kernel(Deco
   const int hq = h / (a.H_v / a.H_qk);  // head repeat (repeat-interleave)
   const int j0 = slice * DVS + c4 * 4;
 
-  // ---- issue the state tile loads first: they are the only large traffic ----
-  float* S = a.state + (static_cast<size_t>(b) * a.H_v + h) * DK * a.dv;
-  float4 s[RPT];
-#pragma unroll
-  for (int m = 0; m < RPT; ++m)
-    s[m] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(row0 + m) * a.dv + j0);
-
-  // ---- Q/K/V split of the packed row ----
+  // ---- every load first: the small per-head inputs, then the state tile ----
+  // Waits are in issue order, so with the small loads ahead of the 64 KiB
+  // tile the norms and gates are computed while the tile is still arriving;
+  // nothing is computed (and so nothing waits) before the tile is requested.
   const IoT* row = static_cast<const IoT*>(a.qkv) +
                    static_cast<size_t>(b) * (2 * a.H_qk * DK + a.H_v * a.dv);
   const IoT* qh = row + hq * DK;
   const IoT* kh = row + a.H_qk * DK + hq * DK;
   const IoT* vh = row + 2 * a.H_qk * DK + h * a.dv;
+  const size_t bh = static_cast<size_t>(b) * a.H_v + h;
 
   float kr[RPT], qr[RPT];
   load_row<IoT, RPT>(kh + row0, kr);
   load_row<IoT, RPT>(qh + row0, qr);
   float vv[4];
   load_row<IoT, 4>(vh + j0, vv);
-
-  // ---- L2 normalisation: every wave reduces the whole head itself ----
-  float inv_nk = 1.0f, inv_nq = 1.0f;
-  if (a.l2norm) {
-    float sk = 0.0f, sq = 0.0f;
-    for (int e = lane; e < DK; e += 64) {
-      float x = to_f32(kh[e]);
-      float y = to_f32(qh[e]);
-      sk += x * x;
-      sq += y * y;
+  float g[kChannel ? RPT : 1];
+  float A_log = 0.0f, dt_bias = 0.0f;
+  if constexpr (kChannel) {
+    load_row<float, RPT>(a.gate_in + bh * DK + row0, g);
+  } else {
+    g[0] = a.gate_in[bh];
+    if (a.gate == GDR_GATE_SCALAR_FUSED) {
+      A_log = a.A_log[h];
+      dt_bias = a.dt_bias[h];
     }
-    sk = wave_sum(sk);
-    sq = wave_sum(sq);
-    inv_nk = 1.0f / sqrtf(sk + kL2Eps);
-    inv_nq = 1.0f / sqrtf(sq + kL2Eps);
+  }
+  const float beta_x = a.beta_logit[bh];
+  // Whole-head k and q for the L2 norms (every wave reduces the head itself);
+  // lanes past dk read element dk - 1 and are masked.
+  constexpr int NE = (DK + 63) / 64;
+  float ek[NE], eq[NE];
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const int e = min(lane + 64 * u, DK - 1);
+    ek[u] = to_f32(kh[e]);
+    eq[u] = to_f32(qh[e]);
   }
 
+  float* S = a.state + bh * DK * a.dv;
+  float4 s[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m)
+    s[m] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(row0 + m) * a.dv + j0);
+
+  // (computed unconditionally, so the element loads stay ahead of the tile)
+  float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const float m = lane + 64 * u < DK ? 1.0f : 0.0f;
+    sk += m * ek[u] * ek[u];
+    sq += m * eq[u] * eq[u];
+  }
+  sk = wave_sum(sk);
+  sq = wave_sum(sq);
+  const float inv_nk = a.l2norm ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
+  const float inv_nq = a.l2norm ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f;
+
   // ---- gates ----
-  const size_t bh = static_cast<size_t>(b) * a.H_v + h;
-  const float beta = sigmoidf(a.beta_logit[bh]);
+  const float beta = sigmoidf(beta_x);
   float ak[RPT], dec[RPT];
-  if (a.gate == GDR_GATE_CHANNEL) {
-    float g[RPT];
-    load_row<float, RPT>(a.gate_in + bh * DK + row0, g);
+  if constexpr (kChannel) {
 #pragma unroll
     for (int m = 0; m < RPT; ++m) dec[m] = expf(g[m]);
   } else {
-    float g = a.gate == GDR_GATE_SCALAR
-                  ? a.gate_in[bh]
-                  : fused_log_decay(a.gate_in[bh], a.A_log[h], a.dt_bias[h]);
-    const float d = expf(g);
+    const float g1 =
+        a.gate == GDR_GATE_SCALAR_FUSED ? fused_log_decay(g[0], A_log, dt_bias) : g[0];
+    const float d = expf(g1);
 #pragma unroll
     for (int m = 0; m < RPT; ++m) dec[m] = d;
   }
@@ -192,8 +211,12 @@ __global__ __launch_bounds__((DecodeShape<DK, DVS>::NT)) void decode_kernel(Deco
 template <typename IoT, int DK, int DVS>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
-  hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS>), dim3(grid), dim3(DecodeShape<DK, DVS>::NT),
-                     0, stream, a);
+  if (a.gate == GDR_GATE_CHANNEL)
+    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, true>), dim3(grid),
+                       dim3(DecodeShape<DK, DVS>::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, false>), dim3(grid),
+                       dim3(DecodeShape<DK, DVS>::NT), 0, stream, a);
   return hipGetLastError();
 }
 

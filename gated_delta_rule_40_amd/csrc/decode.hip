@@ -28,6 +28,22 @@
 namespace gdr {
 namespace {
 
+// The state tile goes through a buffer descriptor (gfx9 family: third word
+// 0x00020000, raw 32-bit elements): one 32-bit lane offset serves every row,
+// and each row's offset is a scalar, so the tile's 16 rows per thread need no
+// per-row 64-bit addresses in vector registers.
+typedef unsigned int u32x4_t __attribute__((__vector_size__(16)));
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ float4 tile_load(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                            unsigned soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                           float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, soff, 0);
+}
+
 template <int DK, int DVS>
 struct DecodeShape {
   static constexpr int C4 = DVS / 4;                          // float4 columns
@@ -41,9 +57,14 @@ struct DecodeShape {
 
 // kChannel: per-channel log-decays; otherwise one per (b, h), plain or fused.
 template <typename IoT, int DK, int DVS, bool kChannel>
-__global__ __launch_bounds__((DecodeShape<DK, DVS>::NT)) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((DecodeShape<DK, DVS>::NT))
+__attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
   using Sh = DecodeShape<DK, DVS>;
   constexpr int C4 = Sh::C4, RPT = Sh::RPT, NW = Sh::NW;
+  constexpr int NE = (DK + 63) / 64;  // head elements per lane of wave 0
+  // Per-row vectors of the head, shared by the C4 lanes of each row group:
+  // normalised k and q, the decay a, and a*k.
+  __shared__ __attribute__((aligned(16))) float kS[DK], qS[DK], dS[DK], akS[DK];
   __shared__ float4 red[2][NW][C4];
 
   const int tid = threadIdx.x;
@@ -60,93 +81,92 @@ __global__ __launch_bounds__((DecodeShape<DK, DVS>::NT)) void decode_kernel(Deco
   const int b = wg / (n_slices * a.H_v);
   const int hq = h / (a.H_v / a.H_qk);  // head repeat (repeat-interleave)
   const int j0 = slice * DVS + c4 * 4;
+  const size_t bh = static_cast<size_t>(b) * a.H_v + h;
 
   // ---- every load first: the small per-head inputs, then the state tile ----
   // Waits are in issue order, so with the small loads ahead of the 64 KiB
-  // tile the norms and gates are computed while the tile is still arriving;
-  // nothing is computed (and so nothing waits) before the tile is requested.
+  // tile the per-head vectors are built while the tile is still arriving.
   const IoT* row = static_cast<const IoT*>(a.qkv) +
                    static_cast<size_t>(b) * (2 * a.H_qk * DK + a.H_v * a.dv);
   const IoT* qh = row + hq * DK;
   const IoT* kh = row + a.H_qk * DK + hq * DK;
   const IoT* vh = row + 2 * a.H_qk * DK + h * a.dv;
-  const size_t bh = static_cast<size_t>(b) * a.H_v + h;
-
-  float kr[RPT], qr[RPT];
-  load_row<IoT, RPT>(kh + row0, kr);
-  load_row<IoT, RPT>(qh + row0, qr);
   float vv[4];
   load_row<IoT, 4>(vh + j0, vv);
-  float g[kChannel ? RPT : 1];
-  float A_log = 0.0f, dt_bias = 0.0f;
-  if constexpr (kChannel) {
-    load_row<float, RPT>(a.gate_in + bh * DK + row0, g);
-  } else {
-    g[0] = a.gate_in[bh];
-    if (a.gate == GDR_GATE_SCALAR_FUSED) {
-      A_log = a.A_log[h];
-      dt_bias = a.dt_bias[h];
-    }
-  }
-  const float beta_x = a.beta_logit[bh];
-  // Whole-head k and q for the L2 norms (every wave reduces the head itself);
-  // lanes past dk read element dk - 1 and are masked.
-  constexpr int NE = (DK + 63) / 64;
-  float ek[NE], eq[NE];
+  const float beta = sigmoidf(a.beta_logit[bh]);
+  // Wave 0 reads the whole head (lanes past dk read element dk - 1, masked).
+  // (every wave loads them, unconditionally, and keeps them raw until the
+  // tile has been requested, so that nothing waits on them before that)
+  IoT rk[NE], rq[NE];
+  float eg[NE];
 #pragma unroll
   for (int u = 0; u < NE; ++u) {
     const int e = min(lane + 64 * u, DK - 1);
-    ek[u] = to_f32(kh[e]);
-    eq[u] = to_f32(qh[e]);
+    rk[u] = kh[e];
+    rq[u] = qh[e];
+    if constexpr (kChannel) eg[u] = a.gate_in[bh * DK + e];
   }
 
+  // The state tile (dk x dv fp32, at most 64 KiB) through a buffer descriptor.
   float* S = a.state + bh * DK * a.dv;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      S, 0, static_cast<int>(DK * a.dv * sizeof(float)), kBufferWord3);
+  const unsigned boff = (static_cast<unsigned>(row0) * a.dv + j0) * 4u;  // lane, bytes
+  const unsigned rstep = static_cast<unsigned>(a.dv) * 4u;                // row, bytes
   float4 s[RPT];
 #pragma unroll
-  for (int m = 0; m < RPT; ++m)
-    s[m] = *reinterpret_cast<const float4*>(S + static_cast<size_t>(row0 + m) * a.dv + j0);
+  for (int m = 0; m < RPT; ++m) s[m] = tile_load(srs, boff, m * rstep);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // (computed unconditionally, so the element loads stay ahead of the tile)
-  float sk = 0.0f, sq = 0.0f;
+  if (wave == 0) {
+    float ek[NE], eq[NE];
 #pragma unroll
-  for (int u = 0; u < NE; ++u) {
-    const float m = lane + 64 * u < DK ? 1.0f : 0.0f;
-    sk += m * ek[u] * ek[u];
-    sq += m * eq[u] * eq[u];
+    for (int u = 0; u < NE; ++u) {
+      ek[u] = to_f32(rk[u]);
+      eq[u] = to_f32(rq[u]);
+    }
+    float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const float msk = lane + 64 * u < DK ? 1.0f : 0.0f;
+      sk += msk * ek[u] * ek[u];
+      sq += msk * eq[u] * eq[u];
+    }
+    sk = wave_sum(sk);
+    sq = wave_sum(sq);
+    const float inv_nk = a.l2norm ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
+    const float inv_nq = a.l2norm ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f;
+    float d1 = 0.0f;
+    if constexpr (!kChannel) {
+      const float g = a.gate == GDR_GATE_SCALAR
+                          ? a.gate_in[bh]
+                          : fused_log_decay(a.gate_in[bh], a.A_log[h], a.dt_bias[h]);
+      d1 = expf(g);
+    }
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = lane + 64 * u;
+      if (e < DK) {
+        const float d = kChannel ? expf(eg[u]) : d1;
+        const float kk = ek[u] * inv_nk;
+        kS[e] = kk;
+        qS[e] = eq[u] * inv_nq;
+        dS[e] = d;
+        akS[e] = d * kk;
+      }
+    }
   }
-  sk = wave_sum(sk);
-  sq = wave_sum(sq);
-  const float inv_nk = a.l2norm ? 1.0f / sqrtf(sk + kL2Eps) : 1.0f;
-  const float inv_nq = a.l2norm ? 1.0f / sqrtf(sq + kL2Eps) : 1.0f;
-
-  // ---- gates ----
-  const float beta = sigmoidf(beta_x);
-  float ak[RPT], dec[RPT];
-  if constexpr (kChannel) {
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) dec[m] = expf(g[m]);
-  } else {
-    const float g1 =
-        a.gate == GDR_GATE_SCALAR_FUSED ? fused_log_decay(g[0], A_log, dt_bias) : g[0];
-    const float d = expf(g1);
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) dec[m] = d;
-  }
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    kr[m] *= inv_nk;
-    qr[m] *= inv_nq;
-    ak[m] = dec[m] * kr[m];
-  }
+  __syncthreads();
 
   // ---- pass 1: vhat = (diag(a) S)^T k ----
   float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
-    p0 += ak[m] * s[m].x;
-    p1 += ak[m] * s[m].y;
-    p2 += ak[m] * s[m].z;
-    p3 += ak[m] * s[m].w;
+    const float ak = akS[row0 + m];  // same address across the row group: broadcast
+    p0 += ak * s[m].x;
+    p1 += ak * s[m].y;
+    p2 += ak * s[m].z;
+    p3 += ak * s[m].w;
   }
 #pragma unroll
   for (int off = C4; off < 64; off <<= 1) {
@@ -173,16 +193,17 @@ __global__ __launch_bounds__((DecodeShape<DK, DVS>::NT)) void decode_kernel(Deco
   float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
+    const float d = dS[row0 + m], kk = kS[row0 + m], qq = qS[row0 + m];
     float4 t = s[m];
-    t.x = dec[m] * t.x + kr[m] * u0;
-    t.y = dec[m] * t.y + kr[m] * u1;
-    t.z = dec[m] * t.z + kr[m] * u2;
-    t.w = dec[m] * t.w + kr[m] * u3;
-    *reinterpret_cast<float4*>(S + static_cast<size_t>(row0 + m) * a.dv + j0) = t;
-    o0 += qr[m] * t.x;
-    o1 += qr[m] * t.y;
-    o2 += qr[m] * t.z;
-    o3 += qr[m] * t.w;
+    t.x = d * t.x + kk * u0;
+    t.y = d * t.y + kk * u1;
+    t.z = d * t.z + kk * u2;
+    t.w = d * t.w + kk * u3;
+    tile_store(srs, boff, m * rstep, t);
+    o0 += qq * t.x;
+    o1 += qq * t.y;
+    o2 += qq * t.z;
+    o3 += qq * t.w;
   }
 #pragma unroll
   for (int off = C4; off < 64; off <<= 1) {

@@ -164,7 +164,7 @@ def bench_decode(K, W, B):
         bytes_per_step=nbytes,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic,
-                      kernel="gdr::decode_kernel<bf16,128,128>",
+                      kernel="gdr::decode_kernel (bf16 io, dk=dv=128, channel gate)",
                       timing="HIP events around the graph replay of all timed steps, / steps",
                       source_digest=digest),
         case=case,

@@ -586,6 +586,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 
 
+// An optional scheduling fence: the compiler does not move instructions across it.
+template <bool kOn>
+__device__ __forceinline__ void pin_order() {
+  if constexpr (kOn) __builtin_amdgcn_sched_barrier(0);
+}
+
 template <typename OpT, int DK, int DVS, int C>
 struct CarryShape {
   using Blk = ChunkBlock<OpT, DK, C>;
@@ -602,6 +608,12 @@ struct CarryShape {
   static constexpr int NOT = (C / 16) * DVT;          // output tiles
   static constexpr int OPW = (NOT + NW - 1) / NW;
   static constexpr size_t kSmem = sizeof(OpT) * (DVS * LDK + 2 * DVS * LDC);
+  // Keep each next-chunk load where it is written (right after the MFMA that
+  // last reads its registers) when a wave owns one output tile; with two the
+  // pinned order costs more registers than it saves (64-column slices:
+  // 3.8 ms against 3.4 ms at B=4, T=32767; 16 columns: 148 us against 166 us
+  // unpinned at B=1, T=4000).
+  static constexpr bool kPinLoads = OPW == 1;
 };
 
 template <typename OpT, int DK, int DVS, int C>
@@ -820,12 +832,14 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
         for (int s = 0; s < FK::STEPS; ++s) {
           if (s + 1 < FK::STEPS) z[s + 1] = FK::load_pad(St_s, LDK, 16 * J, s + 1, lane);
           ks = FK::mma(F.kt[i][s], z[s], ks);
-          oacc[i] = FK::mma(F.qt[i][s], z[s], oacc[i]);
-          // The next chunk's fragments go out one pair per step, so the CU's
-          // load path is fed steadily instead of in a burst that stalls issue.
+          // O is accumulated transposed (S^T Qt^T): each lane then holds four
+          // consecutive columns of one output row, stored with one wide write.
+          oacc[i] = FK::mma(z[s], F.qt[i][s], oacc[i]);
+          // The next chunk's fragments go out one pair per step, each as soon
+          // as its registers have been read.
           F.kt[i][s] = FK::load(nblk + Blk::kKt, 16 * R, s, lane);
           F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
-          __builtin_amdgcn_sched_barrier(0);
+          pin_order<Sh::kPinLoads>();
         }
         float rv[4];
 #pragma unroll
@@ -850,7 +864,7 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
         for (int s = 0; s < FC::STEPS; ++s) {
           u = FC::mma(F.tb[i][s], FC::load_pad(Rt_s, LDC, 16 * J, s, lane), u);
           F.tb[i][s] = FC::load(nblk + Blk::kTb, 16 * R, s, lane);
-          __builtin_amdgcn_sched_barrier(0);
+          pin_order<Sh::kPinLoads>();
         }
         float uv[4] = {u[0], u[1], u[2], u[3]};
         store_tile_t<OpT>(Ut_s, LDC, 16 * J, 16 * R, uv, lane);
@@ -866,23 +880,9 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
         const int R = t / DVT, J = t % DVT;
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s) {
-          oacc[i] = FC::mma(F.p[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), oacc[i]);
+          oacc[i] = FC::mma(FC::load_pad(Ut_s, LDC, 16 * J, s, lane), F.p[i][s], oacc[i]);
           F.p[i][s] = FC::load(nblk + Blk::kP, 16 * R, s, lane);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        OpT* obase = og + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
-        const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
-        const unsigned r0 = 16 * R + 4 * (lane >> 4);
-        const unsigned col = 16 * J + (lane & 15);
-        if constexpr (kFull) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            obase[(r0 + e) * rs + col] = from_f32<OpT>(a.scale * oacc[i][e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (static_cast<int>(r0) + e < L)
-              obase[(r0 + e) * rs + col] = from_f32<OpT>(a.scale * oacc[i][e]);
+          pin_order<Sh::kPinLoads>();
         }
       }
     }
@@ -899,8 +899,28 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
         for (int s = 0; s < FC::STEPS; ++s) {
           sacc[i] = FC::mma(F.ke[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), sacc[i]);
           F.ke[i][s] = FC::load(nblk + Blk::kKeT, 16 * I, s, lane);
-          __builtin_amdgcn_sched_barrier(0);
+          pin_order<Sh::kPinLoads>();
         }
+      }
+    }
+    // The o rows go out last, after every load of the step.  On gfx9 stores
+    // and loads share one in-order completion counter, so a wait for a load
+    // issued after a store also waits for that store's write acknowledgement;
+    // with the stores last, the first load issued after them is waited for
+    // two chunk steps later.
+#pragma unroll
+    for (int i = 0; i < OPW; ++i) {
+      const int t = wave * OPW + i;
+      if (NOT % Sh::NW == 0 || t < NOT) {
+        const int R = t / DVT, J = t % DVT;
+        // lane (c, g): row 16 R + c, columns 16 J + 4 g ... + 3 of the chunk's o
+        OpT* obase = og + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
+        const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
+        const int r = 16 * R + (lane & 15);
+        OpT* op = obase + (static_cast<unsigned>(r) * rs + 16 * J + 4 * (lane >> 4));
+        if (kFull || r < L)
+          store4<OpT>(op, a.scale * oacc[i][0], a.scale * oacc[i][1], a.scale * oacc[i][2],
+                      a.scale * oacc[i][3]);
       }
     }
   };

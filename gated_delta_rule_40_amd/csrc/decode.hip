@@ -94,9 +94,9 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
   float vv[4];
   load_row<IoT, 4>(vh + j0, vv);
   const float beta = sigmoidf(a.beta_logit[bh]);
-  // Wave 0 reads the whole head (lanes past dk read element dk - 1, masked).
-  // (every wave loads them, unconditionally, and keeps them raw until the
-  // tile has been requested, so that nothing waits on them before that)
+  // Every wave reads the whole head's k and q (lanes past dk read element
+  // dk - 1, masked) and keeps them raw until the tile has been requested, so
+  // that nothing waits on them before that.
   IoT rk[NE], rq[NE];
   float eg[NE];
 #pragma unroll
@@ -118,7 +118,10 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
   for (int m = 0; m < RPT; ++m) s[m] = tile_load(srs, boff, m * rstep);
   __builtin_amdgcn_sched_barrier(0);
 
-  if (wave == 0) {
+  // Every wave builds the whole head's vectors and writes them to the same
+  // LDS words; the values are identical, and each wave reads only after its
+  // own writes, so no barrier is needed before pass 1.
+  {
     float ek[NE], eq[NE];
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
@@ -156,7 +159,8 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
 
   // ---- pass 1: vhat = (diag(a) S)^T k ----
   float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;

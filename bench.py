@@ -149,6 +149,7 @@ def bench_decode(K, W, B):
 
     kern_s = graph_ms / K / 1e3          # average launch duration inside the replay
     achieved = nbytes / kern_s / 1e9
+    ceiling = inplace_ceiling(S, K)
     digest = source_digest("decode.hip")
     traffic = traffic_from_profile(f"decode_b{B}", digest)
     return dict(
@@ -166,9 +167,41 @@ def bench_decode(K, W, B):
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic,
                       kernel="gdr::decode_kernel (bf16 io, dk=dv=128, channel gate)",
                       timing="HIP events around the graph replay of all timed steps, / steps",
-                      source_digest=digest),
+                      source_digest=digest,
+                      inplace_ceiling=dict(ceiling, frac=achieved / ceiling["gbs"])),
         case=case,
     )
+
+
+def inplace_ceiling(S, K):
+    """The practical ceiling of an in-place state update: torch's own elementwise
+    kernel scaling the same fp32 state buffer in place (read + write of every
+    byte, random values), K launches captured in a graph like the decode steps.
+    The factors alternate between 2 and 1/2 over an even number of launches,
+    which is exact, so S comes back unchanged.  Memory traffic on this part depends on the values moved (an
+    all-zero buffer streams markedly faster), so the ceiling is taken on the
+    state itself."""
+    n = K + K % 2
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(n):
+                S.mul_(2.0 if i % 2 == 0 else 0.5)
+    torch.cuda.current_stream().wait_stream(cap)
+    graph.replay()                       # warm replay
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    nbytes = 2 * S.numel() * S.element_size()
+    del graph
+    return dict(gbs=nbytes / us / 1e3, us=us, bytes=nbytes,
+                kernel="torch in-place mul_ on the fp32 state (graph replay)")
 
 
 def cpu_decode(case, seconds):

@@ -215,6 +215,13 @@ struct PrepSmem {
   static constexpr size_t oR1 = al16(mx(mx(kOpRows, kN), kX));
   static constexpr size_t oR2 = oR1 + al16(mx(kOpRows, kTm));
   static constexpr size_t kBytes = oR2 + al16(mx(kTm, kG));
+  static constexpr size_t oBeta = kBytes;  // beta of the chunk's rows
+  static constexpr size_t kAll = kBytes + al16(static_cast<size_t>(C) * sizeof(float));
+};
+
+// A half-open range [n0, n1) of chunk indices.
+struct ChunkRange {
+  int n0, n1;
 };
 
 // Element offset of (row, col) in a region held in fragment order.
@@ -248,15 +255,17 @@ __device__ __forceinline__ void frag_store(OpT* region, int row, int col0, const
 
 // kChannel: per-channel log-decays (one per key channel and row); otherwise one
 // per row (plain or fused), broadcast over the channels.
+// One work unit (b, h, chunk) per workgroup, over the chunks of cr; wg is the
+// workgroup's index among the G that do this work, and sm its LDS (kAll bytes).
 template <typename OpT, int DK, int C, bool kChannel>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, int wg, int G,
+                                          unsigned char* sm) {
   using Sm = PrepSmem<OpT, DK, C>;
   using Blk = ChunkBlock<OpT, DK, C>;
   constexpr int LDK = Sm::LDK, LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
   constexpr int PARTS = Sm::PARTS, RPP = Sm::RPP;
 
-  __shared__ __attribute__((aligned(16))) unsigned char sm[Sm::kBytes];
-  __shared__ float beta_s[C];
+  float* beta_s = reinterpret_cast<float*>(sm + Sm::oBeta);
 
   OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);
   OpT* Qt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);     // after A
@@ -270,17 +279,17 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int NC = (a.T + C - 1) / C;
+  const int NCr = cr.n1 - cr.n0;
   // Work order: the rep = H_v / H_qk value heads that share a qk head, for one
   // chunk, are consecutive units, and consecutive units run on one XCD
   // (workgroups w, w + 8, ... share an XCD), so all but the first read that
   // chunk's q and k rows from the XCD's L2.
-  const int G = gridDim.x;
-  int unit = blockIdx.x;
-  if (G % 8 == 0) unit = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  int unit = wg;
+  if (G % 8 == 0) unit = (wg % 8) * (G / 8) + wg / 8;
   const int rep = a.H_v / a.H_qk;
   const int r_in = unit % rep;
-  const int n = (unit / rep) % NC;
-  const int bq = unit / (rep * NC);  // b * H_qk + hq
+  const int n = cr.n0 + (unit / rep) % NCr;
+  const int bq = unit / (rep * NCr);  // b * H_qk + hq
   const int hq = bq % a.H_qk;
   const int b = bq / a.H_qk;
   const int h = hq * rep + r_in;
@@ -569,6 +578,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a) {
   }
 }
 
+template <typename OpT, int DK, int C, bool kChannel>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, ChunkRange cr) {
+  __shared__ __attribute__((aligned(16))) unsigned char sm[PrepSmem<OpT, DK, C>::kAll];
+  prep_body<OpT, DK, C, kChannel>(a, cr, blockIdx.x, gridDim.x, sm);
+}
+
 // ---------------------------------------------------------------------------
 // chunk_carry
 //
@@ -736,9 +751,13 @@ __device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C>& F,
   carry_load<OpT, DK, DVS, C, 2>(F, a, ws_head, nn, b, h, jb, wave, lane);
 }
 
+// One workgroup per (b, h, slice), over the chunks of cr: the state slice
+// starts from s_src (zeros when it is null) and ends in state_out.  wg is the
+// workgroup's index among the G that do this work, and sm its LDS (kSmem bytes).
 template <typename OpT, int DK, int DVS, int C>
-__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry_kernel(
-    PrefillArgs a) {
+__device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
+                                           const float* s_src, int wg, int G,
+                                           unsigned char* sm) {
   using Sh = CarryShape<OpT, DK, DVS, C>;
   using Blk = typename Sh::Blk;
   using FK = typename Sh::FK;
@@ -747,9 +766,9 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   constexpr int LDK = Sh::LDK, LDC = Sh::LDC, DVT = Sh::DVT;
   constexpr int SPW = Sh::SPW, OPW = Sh::OPW, NST = Sh::NST, NOT = Sh::NOT;
 
-  __shared__ __attribute__((aligned(16))) OpT St_s[DVS * LDK];
-  __shared__ __attribute__((aligned(16))) OpT Rt_s[DVS * LDC];
-  __shared__ __attribute__((aligned(16))) OpT Ut_s[DVS * LDC];
+  OpT* St_s = reinterpret_cast<OpT*>(sm);
+  OpT* Rt_s = St_s + DVS * LDK;
+  OpT* Ut_s = Rt_s + DVS * LDC;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -759,9 +778,8 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   // XCD-aware order: workgroups w, w+8, w+16, ... run on one XCD (and share its
   // L2); give them consecutive (head, slice) units so that the slices of one
   // head read that head's chunk blocks through the same L2.
-  const int G = gridDim.x;
-  int unit = blockIdx.x;
-  if (G % 8 == 0) unit = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  int unit = wg;
+  if (G % 8 == 0) unit = (wg % 8) * (G / 8) + wg / 8;
   const int slice = unit % n_sl;
   const int bh = unit / n_sl;
   const int h = bh % a.H_v;
@@ -780,12 +798,12 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   for (int i = 0; i < SPW; ++i) {
     const int t = wave * SPW + i;
     sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if ((NST % Sh::NW == 0 || t < NST) && a.state_in) {
+    if ((NST % Sh::NW == 0 || t < NST) && s_src) {
       const int I = t / DVT, J = t % DVT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * I + 4 * (lane >> 4) + e;
-        sacc[i][e] = a.state_in[st_off + static_cast<size_t>(row) * a.dv + jb + 16 * J +
+        sacc[i][e] = s_src[st_off + static_cast<size_t>(row) * a.dv + jb + 16 * J +
                                 (lane & 15)];
       }
     }
@@ -794,7 +812,7 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   // One register set of fragments: as soon as a phase has consumed its
   // fragments, the same registers start loading that phase's fragments of
   // the next chunk, so each load has most of a chunk step to arrive.  The
-  // last chunk re-reads itself (in bounds, unused), keeping every load
+  // range's last chunk re-reads itself (in bounds, unused), keeping every load
   // unconditional so that the wait counters stay exact across iterations.
   // kFull: the chunk has all C rows (every chunk but a ragged last one), so
   // the o stores need no row guard and the loop body holds no branch around
@@ -803,7 +821,7 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
     constexpr bool kFull = decltype(full)::value;
     const int t0 = nn * C;
     const int L = kFull ? C : min(C, a.T - t0);
-    const int nx = min(nn + 1, NC - 1);
+    const int nx = min(nn + 1, cr.n1 - 1);
     const OpT* nblk = reinterpret_cast<const OpT*>(ws_head + static_cast<size_t>(nx) * Blk::kBytes);
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll
@@ -926,10 +944,11 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   };
 
   Frags F;
-  carry_load_all<OpT, DK, DVS, C>(F, a, ws_head, 0, b, h, jb, wave, lane);
+  carry_load_all<OpT, DK, DVS, C>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
   const int NF = a.T / C;  // full chunks
-  for (int nn = 0; nn < NF; ++nn) compute(F, nn, std::true_type{});
-  if (NF < NC) compute(F, NF, std::false_type{});
+  const int nf_end = min(cr.n1, NF);
+  for (int nn = cr.n0; nn < nf_end; ++nn) compute(F, nn, std::true_type{});
+  if (cr.n1 > NF) compute(F, NF, std::false_type{});  // the ragged last chunk
 
   // ---- final state ----
 #pragma unroll
@@ -946,6 +965,14 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
     }
   }
 }
+
+template <typename OpT, int DK, int DVS, int C>
+__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry_kernel(
+    PrefillArgs a, ChunkRange cr, const float* s_src) {
+  __shared__ __attribute__((aligned(16))) unsigned char sm[CarryShape<OpT, DK, DVS, C>::kSmem];
+  carry_body<OpT, DK, DVS, C>(a, cr, s_src, blockIdx.x, gridDim.x, sm);
+}
+
 
 // T = 0: state_out = state_in (or zeros).
 __global__ void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
@@ -976,10 +1003,11 @@ size_t block_bytes_rt(int dk, int chunk) {
 }
 
 template <typename OpT, int DK, int DVS, int C>
-hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_carry(const PrefillArgs& a, ChunkRange cr, const float* s_src,
+                        hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
   hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C>), dim3(grid),
-                     dim3(CarryShape<OpT, DK, DVS, C>::NT), 0, stream, a);
+                     dim3(CarryShape<OpT, DK, DVS, C>::NT), 0, stream, a, cr, s_src);
   return hipGetLastError();
 }
 
@@ -989,31 +1017,41 @@ hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
 // workgroup costs more the wider its slice, but a second workgroup on a CU
 // costs more still: the carry is a chain of dependent steps, so two chains
 // sharing a CU's load path and matrix cores each run slower.
-template <typename OpT, int DK, int C>
-hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
+int carry_slice_width(const PrefillArgs& a) {
   const long units = static_cast<long>(a.B) * a.H_v;
   int dvs = a.dv < 16 ? a.dv : 16;
   while (dvs < a.dv && dvs < 64 && units * (a.dv / dvs) > 256) dvs *= 2;
-  switch (dvs) {
-    case 16: return launch_carry<OpT, DK, 16, C>(a, stream);
-    case 32: return launch_carry<OpT, DK, 32, C>(a, stream);
-    default: return launch_carry<OpT, DK, 64, C>(a, stream);
+  return dvs;
+}
+
+template <typename OpT, int DK, int C>
+hipError_t launch_carry_any(const PrefillArgs& a, ChunkRange cr, const float* s_src,
+                            hipStream_t stream) {
+  switch (carry_slice_width(a)) {
+    case 16: return launch_carry<OpT, DK, 16, C>(a, cr, s_src, stream);
+    case 32: return launch_carry<OpT, DK, 32, C>(a, cr, s_src, stream);
+    default: return launch_carry<OpT, DK, 64, C>(a, cr, s_src, stream);
   }
 }
 
 template <typename OpT, int DK, int C>
-hipError_t launch_dk_c(const PrefillArgs& a, hipStream_t stream) {
-  const int NC = (a.T + C - 1) / C;
-  const unsigned prep_grid = static_cast<unsigned>(a.B) * a.H_v * NC;
+hipError_t launch_prep(const PrefillArgs& a, ChunkRange cr, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (cr.n1 - cr.n0);
   if (a.gate == GDR_GATE_CHANNEL)
-    hipLaunchKernelGGL((chunk_prep_kernel<OpT, DK, C, true>), dim3(prep_grid), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((chunk_prep_kernel<OpT, DK, C, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, a, cr);
   else
-    hipLaunchKernelGGL((chunk_prep_kernel<OpT, DK, C, false>), dim3(prep_grid), dim3(kThreads), 0,
-                       stream, a);
-  hipError_t err = hipGetLastError();
+    hipLaunchKernelGGL((chunk_prep_kernel<OpT, DK, C, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, a, cr);
+  return hipGetLastError();
+}
+
+template <typename OpT, int DK, int C>
+hipError_t launch_dk_c(const PrefillArgs& a, hipStream_t stream) {
+  const ChunkRange all{0, (a.T + C - 1) / C};
+  const hipError_t err = launch_prep<OpT, DK, C>(a, all, stream);
   if (err != hipSuccess) return err;
-  return launch_carry_any<OpT, DK, C>(a, stream);
+  return launch_carry_any<OpT, DK, C>(a, all, a.state_in, stream);
 }
 
 template <typename OpT, int DK>

@@ -146,6 +146,34 @@ def test_prefill_t32767_b4_sampled(gate):
     assert worst_o < TOL["bf16"] and worst_s < TOL["bf16"]
 
 
+# Long sequences at few (b, h) units: 25 to 61 chunks of 16 (ragged last
+# chunk) and 25 of 64, with a nonzero, a null and an in-place initial state.
+@pytest.mark.parametrize("T,chunk,gate,mode", [
+    (389, 16, synth.GATE_CHANNEL, "S0"),
+    (600, 16, synth.GATE_CHANNEL, "S0"),
+    (967, 16, synth.GATE_CHANNEL, "S0"),
+    (600, 16, synth.GATE_SCALAR_FUSED, "S0"),
+    (600, 16, synth.GATE_CHANNEL, "inplace"),
+    (600, 16, synth.GATE_CHANNEL, "null"),
+    (1600, 64, synth.GATE_CHANNEL, "bf16"),
+])
+def test_prefill_long_few_heads(T, chunk, gate, mode):
+    require_gpu()
+    io = "bf16" if mode == "bf16" else "f32"
+    dkv = 64 if mode == "bf16" else 32
+    s0 = 0.0 if mode == "null" else 0.4
+    case = synth.prefill_case(f"long{T}", 70 + T % 17, 1, T, 2, 4, dkv, dkv, chunk, io, gate,
+                              0.01, 0.3, s0)
+    announce(f"prefill long io={io} T={T} chunk={chunk} gate={gate} {mode} B=1 H 2->4 "
+             f"dk=dv={dkv}")
+    kw = {"inplace": True} if mode == "inplace" else ({"state_in": None} if mode == "null" else {})
+    o, S = run_prefill(case, **kw)
+    o_ref, S_ref = _oracle(case)
+    eo, es = rel(o, o_ref), rel(S, S_ref)
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[io] and es < TOL[io]
+
+
 def test_prefill_split_sequence_equals_whole():
     require_gpu()
     case = synth.prefill_case("split", 61, 2, 150, 2, 2, 64, 64, 32, "f32", synth.GATE_CHANNEL,

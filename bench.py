@@ -292,6 +292,100 @@ def bench_prefill(reps, warm):
     )
 
 
+# ---------------------------------------------------------------------------
+# T-sweep: T decode steps against one chunked prefill of the same T tokens
+# ---------------------------------------------------------------------------
+SWEEP_TS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4000)
+
+
+def graph_us(fn, reps=5):
+    """Capture fn once in a HIP graph and time its replays with HIP events
+    (replays run on the current stream, where the events are recorded)."""
+    fn()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            fn()
+    torch.cuda.current_stream().wait_stream(cap)
+    graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def bench_sweep(batches=(1, 16), ts=SWEEP_TS, seed=11):
+    """For each batch B and length T: T consecutive gdr_decode_step calls (one
+    token each, graph-replayed as a serving loop would issue them) against one
+    gdr_prefill_chunked over the same T tokens, both from the same initial
+    state.  H_qk=16 -> H_v=32, dk=dv=128, bf16 io, channelwise gate, chunk 64,
+    inputs drawn on the device from a seeded generator (q, k, v ~ N(0,1),
+    g ~ -U(0.001, 0.2), beta logits ~ N(0,1), S0 ~ N(0, 0.02)).  `agree` is
+    max|o_prefill - o_decode| / max|o_decode| over the T outputs."""
+    H_qk, H_v, dk, dv, C = 16, 32, 128, 128, 64
+    gate = synth.GATE_CHANNEL
+    kw = dict(H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, gate=gate)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    out = []
+    for B in batches:
+        pts = []
+        for T in ts:
+            bf = torch.bfloat16
+            q = torch.randn(B, T, H_qk, dk, device=DEV, generator=gen).to(bf)
+            k = torch.randn(B, T, H_qk, dk, device=DEV, generator=gen).to(bf)
+            v = torch.randn(B, T, H_v, dv, device=DEV, generator=gen).to(bf)
+            g = -(torch.rand(B, T, H_v, dk, device=DEV, generator=gen) * 0.199 + 0.001)
+            bl = torch.randn(B, T, H_v, device=DEV, generator=gen)
+            S0 = torch.randn(B, H_v, dk, dv, device=DEV, generator=gen) * 0.02
+            # the decode path's per-token inputs: packed q|k|v rows, gates, beta
+            qkv = torch.cat([q.transpose(0, 1).reshape(T, B, -1), k.transpose(0, 1).reshape(T, B, -1),
+                             v.transpose(0, 1).reshape(T, B, -1)], dim=2).contiguous()
+            gd = g.transpose(0, 1).contiguous()
+            bd = bl.transpose(0, 1).contiguous()
+            Sd = S0.clone()
+            od = torch.empty((T, B, H_v, dv), dtype=bf, device=DEV)
+            Sp = torch.empty_like(S0)
+            op = torch.empty((B, T, H_v, dv), dtype=bf, device=DEV)
+            ws = torch.empty(gdr.gdr_prefill_workspace_size(B, T, H_qk, H_v, dk, dv, C, bf, gate),
+                             dtype=torch.uint8, device=DEV)
+
+            def decode_all():
+                for i in range(T):
+                    gdr.gdr_decode_step(qkv[i], gd[i], bd[i], Sd, od[i], **kw)
+
+            def prefill_all():
+                gdr.gdr_prefill_chunked(q, k, v, g, bl, S0, Sp, op, ws, chunk=C, **kw)
+
+            Sd.copy_(S0)
+            decode_all()
+            prefill_all()
+            torch.cuda.synchronize()
+            ref = od.transpose(0, 1).float()
+            agree = float((op.float() - ref).abs().max() / ref.abs().max().clamp_min(1e-30))
+            reps = 3 if B * T >= 16384 else 10
+            du = graph_us(decode_all, reps)
+            pu = graph_us(prefill_all, reps)
+            pts.append(dict(T=T, decode_us=du, prefill_us=pu, decode_tok_s=B * T / du * 1e6,
+                            prefill_tok_s=B * T / pu * 1e6, agree=agree))
+            print(f"[bench] sweep B={B} T={T}: decode {du:.1f} us, prefill {pu:.1f} us, "
+                  f"agree {agree:.1e}", file=sys.stderr, flush=True)
+            del q, k, v, g, bl, S0, qkv, gd, bd, Sd, od, Sp, op, ws
+            torch.cuda.empty_cache()
+        cross = next((p["T"] for p in pts if p["prefill_us"] < p["decode_us"]), None)
+        out.append(dict(B=B, crossover_T=cross, points=pts))
+    return dict(config="H_qk=16->H_v=32, dk=dv=128, bf16 io, channelwise gate, chunk 64, "
+                       "S0 ~ N(0, 0.02); decode steps graph-replayed, prefill graph-replayed",
+                batches=out)
+
+
 def cpu_prefill(case, seconds):
     import oracle
 
@@ -342,7 +436,9 @@ def main():
     ap.add_argument("--batch", type=int, default=64, help="decode batch (64 is the workload)")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=3)
-    ap.add_argument("--legs", default="decode,prefill")
+    ap.add_argument("--legs", default="decode,prefill",
+                    help="comma list of decode, prefill, sweep (T-sweep of decode steps against "
+                         "one prefill), copy (HBM-counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time box of each CPU-oracle baseline (0 disables)")
     args = ap.parse_args()
@@ -366,6 +462,11 @@ def main():
     if "prefill" in legs:
         pre = bench_prefill(args.prefill_reps, args.prefill_warmup)
         print(f"[bench] prefill done: {pre['value']:.3e} tok/s", file=sys.stderr, flush=True)
+
+    sweep = None
+    if "sweep" in legs:
+        sweep = bench_sweep()
+        print("[bench] sweep done", file=sys.stderr, flush=True)
 
     if "copy" in legs:
         n = copy_calibration()
@@ -406,6 +507,8 @@ def main():
                         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                         "data": "synthetic", "config": {"workload": pre["workload"]},
                         "roofline": pre["roofline"], "cpu_baseline": cpu_pre})
+    if sweep is not None:
+        out["sweep"] = sweep
     print(json.dumps(out), flush=True)
 
 

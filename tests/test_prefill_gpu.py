@@ -213,6 +213,31 @@ def test_prefill_t1_equals_decode():
     assert rel(o_p[:, 0], to_host(o)) < 1e-5 and rel(S_p, to_host(S)) < 1e-5
 
 
+@pytest.mark.parametrize("gate", [synth.GATE_CHANNEL, synth.GATE_SCALAR_FUSED])
+def test_prefill_equals_decode_steps(gate):
+    """One prefill over T=37 tokens (chunk 16: 2 full chunks + 5) against 37
+    consecutive decode steps from the same state, fp32 io: outputs and final
+    state agree to the fp32 tolerance."""
+    require_gpu()
+    T, B, H_qk, H_v, d = 37, 2, 2, 4, 32
+    case = synth.prefill_case("pd", 66, B, T, H_qk, H_v, d, d, 16, "f32", gate, 0.01, 0.3, 0.4)
+    announce(f"prefill T=37 vs 37 decode steps, gate={gate}")
+    o_p, S_p = run_prefill(case)
+    t = case.tensors
+    S = to_dev(t["S0"])
+    o = torch.empty((B, H_v, d), device=DEV)
+    o_d = np.empty((B, T, H_v, d))
+    for i in range(T):
+        qkv = np.concatenate([t["q"][:, i].reshape(B, -1), t["k"][:, i].reshape(B, -1),
+                              t["v"][:, i].reshape(B, -1)], axis=1)
+        gdr.gdr_decode_step(to_dev(qkv), to_dev(t["gate_in"][:, i]), to_dev(t["beta_logit"][:, i]),
+                            S, o, H_qk=H_qk, H_v=H_v, dk=d, dv=d, gate=gate,
+                            A_log=to_dev(t["A_log"]), dt_bias=to_dev(t["dt_bias"]))
+        o_d[:, i] = to_host(o)
+    S_d = to_host(S)
+    assert rel(o_p, o_d) < TOL["f32"] and rel(S_p, S_d) < TOL["f32"]
+
+
 def test_prefill_inplace_state():
     require_gpu()
     case = synth.prefill_case("inplace", 64, 2, 100, 1, 2, 32, 32, 32, "f32", synth.GATE_CHANNEL,

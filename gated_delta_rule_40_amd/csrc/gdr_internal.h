@@ -51,4 +51,14 @@ struct PrefillArgs {
 size_t prefill_workspace_bytes(int B, int T, int H_v, int dk, int dv, int chunk, int io_bf16);
 hipError_t launch_prefill(const PrefillArgs& a, int io_bf16, hipStream_t stream);
 
+// Short sequences token by token (the state tile held in registers over all
+// T tokens; the workspace is not used).  The prefill takes this path for
+// T <= recurrent_max_t(B, H_v) when the per-token vectors fit
+// kRecurrentMaxLds bytes of LDS per workgroup.
+constexpr size_t kRecurrentMaxLds = 64 * 1024;
+int recurrent_max_t(int B, int H_v);
+int recurrent_dv_slice(int B, int H_v, int dv);
+size_t recurrent_lds_bytes(int T, int dk, int dv_slice);
+hipError_t launch_recurrent(const PrefillArgs& a, int io_bf16, hipStream_t stream);
+
 }  // namespace gdr

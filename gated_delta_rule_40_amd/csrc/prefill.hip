@@ -1094,6 +1094,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int io_bf16, hipStream_t stream)
                        a.state_out, n);
     return hipGetLastError();
   }
+  if (a.T <= recurrent_max_t(a.B, a.H_v) &&
+      recurrent_lds_bytes(a.T, a.dk, recurrent_dv_slice(a.B, a.H_v, a.dv)) <= kRecurrentMaxLds)
+    return launch_recurrent(a, io_bf16, stream);
   return io_bf16 ? launch_io<bf16>(a, stream) : launch_io<float>(a, stream);
 }
 

@@ -134,6 +134,12 @@ size_t gdr_prefill_workspace_size(const gdr_dims* dims, gdr_dtype io, gdr_gate g
  * disjoint slice of the caller's workspace.  The result equals T applications
  * of the token update (up to rounding).
  *
+ * Short sequences (T <= 16 at up to 64 (batch, head) units, T <= 24 above)
+ * are run token by token instead, each token the two-pass update above, with
+ * the state held on chip across the tokens: the fixed cost of the chunked form
+ * does not pay off there.  The workspace is then not touched, but the same
+ * size is still required.
+ *
  *   dims        B, T, H_qk, H_v, dk, dv, chunk
  *   io          dtype of q, k, v and o
  *   gate        see gdr_gate; gate_in shape [B,T,H_v,dk] or [B,T,H_v]

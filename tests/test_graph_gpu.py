@@ -1,4 +1,4 @@
-"""Decode steps and a chunked prefill captured in a HIP graph: every replay
+"""Decode steps and prefills (chunked and token-by-token) captured in a HIP graph: every replay
 must reproduce the eager result exactly (same kernels, same inputs).  The
 replays are separated by eager work and synchronisation."""
 from __future__ import annotations
@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 def test_graph_replays_match_eager():
     require_gpu()
-    announce("graph capture: 6 decode steps (B=4) + one prefill (T=100), 3 replays")
+    announce("graph capture: 6 decode steps (B=4) + prefills T=100 and T=9, 3 replays")
     dec = synth.decode_case("graph", 71, 4, 6, 2, 4, 64, 64, "bf16", synth.GATE_CHANNEL,
                             0.01, 0.5, 0.3)
     td = dec.tensors
@@ -35,17 +35,30 @@ def test_graph_replays_match_eager():
     ws = new_workspace(2, 100, 2, 4, 64, 64, 32, "bf16", synth.GATE_SCALAR)
     pkw = dict(H_qk=2, H_v=4, dk=64, dv=64, chunk=32, gate=synth.GATE_SCALAR)
 
+    # a short prefill (token-by-token path), its state carried in place
+    sh = synth.prefill_case("graph_s", 73, 2, 9, 2, 4, 64, 64, 16, "bf16", synth.GATE_CHANNEL,
+                            0.01, 0.3, 0.3)
+    ts = sh.tensors
+    sq, sk, sv = to_dev(ts["q"]), to_dev(ts["k"]), to_dev(ts["v"])
+    sg, sb, ss0 = to_dev(ts["gate_in"]), to_dev(ts["beta_logit"]), to_dev(ts["S0"])
+    ss = ss0.clone()
+    so = torch.empty((2, 9, 4, 64), dtype=torch.bfloat16, device=DEV)
+    sws = new_workspace(2, 9, 2, 4, 64, 64, 16, "bf16", synth.GATE_CHANNEL)
+    skw = dict(H_qk=2, H_v=4, dk=64, dv=64, chunk=16, gate=synth.GATE_CHANNEL)
+
     def work():
         for i in range(6):
             gdr.gdr_decode_step(qkv[i], g[i], bl[i], S, o, **kw)
         gdr.gdr_prefill_chunked(pq, pk, pv, pg, pb, ps0, ps, po, ws, **pkw)
+        gdr.gdr_prefill_chunked(sq, sk, sv, sg, sb, ss, ss, so, sws, **skw)
 
     work()
     torch.cuda.synchronize()
-    ref = (S.clone(), o.clone(), ps.clone(), po.clone())
+    ref = (S.clone(), o.clone(), ps.clone(), po.clone(), ss.clone(), so.clone())
 
     graph = torch.cuda.CUDAGraph()
     S.copy_(S0)
+    ss.copy_(ss0)
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
@@ -55,11 +68,13 @@ def test_graph_replays_match_eager():
     torch.cuda.synchronize()
     for rep in range(3):
         S.copy_(S0)            # eager work between replays
+        ss.copy_(ss0)
         ps.zero_()
         po.zero_()
+        so.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = (S, o, ps, po)
+        got = (S, o, ps, po, ss, so)
         for a, b in zip(got, ref):
             assert torch.equal(a, b), f"replay {rep} differs from eager"

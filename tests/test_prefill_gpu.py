@@ -146,6 +146,50 @@ def test_prefill_t32767_b4_sampled(gate):
     assert worst_o < TOL["bf16"] and worst_s < TOL["bf16"]
 
 
+# Short sequences (T <= 16 at up to 64 (b, h) units, T <= 24 above) take the
+# token-by-token path; the cases cover every head size, gate kind and state
+# mode, both io dtypes, and slices of 16 to 128 state columns.
+@pytest.mark.parametrize("T,B,H_qk,H_v,dk,dv,gate,io,mode", [
+    (2, 1, 2, 4, 32, 32, synth.GATE_CHANNEL, "f32", "S0"),
+    (5, 2, 1, 2, 16, 128, synth.GATE_SCALAR, "f32", "S0"),
+    (16, 1, 2, 4, 128, 32, synth.GATE_SCALAR_FUSED, "f32", "S0"),
+    (13, 3, 2, 2, 64, 16, synth.GATE_CHANNEL, "f32", "inplace"),
+    (12, 2, 2, 4, 64, 64, synth.GATE_CHANNEL, "f32", "null"),
+    (16, 1, 16, 32, 128, 128, synth.GATE_CHANNEL, "bf16", "S0"),
+    (24, 4, 16, 32, 128, 128, synth.GATE_SCALAR, "bf16", "S0"),
+    (8, 16, 16, 32, 128, 128, synth.GATE_CHANNEL, "bf16", "S0"),
+])
+def test_prefill_short_token_path(T, B, H_qk, H_v, dk, dv, gate, io, mode):
+    require_gpu()
+    s0 = 0.0 if mode == "null" else 0.4
+    case = synth.prefill_case(f"short{T}", 80 + T, B, T, H_qk, H_v, dk, dv, 16, io, gate,
+                              0.01, 0.3, s0)
+    announce(f"prefill short io={io} T={T} B={B} H {H_qk}->{H_v} dk={dk} dv={dv} gate={gate} "
+             f"{mode}")
+    kw = {"inplace": True} if mode == "inplace" else ({"state_in": None} if mode == "null" else {})
+    o, S = run_prefill(case, **kw)
+    o_ref, S_ref = _oracle(case)
+    eo, es = rel(o, o_ref), rel(S, S_ref)
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[io] and es < TOL[io]
+
+
+@pytest.mark.parametrize("T", [24, 25])
+def test_prefill_short_path_boundary(T):
+    """B=8, H 16 -> 32, dk=dv=128, bf16, chunk 64: T=24 is the last length on
+    the token-by-token path at 256 (b, h) units, T=25 one ragged chunk on the
+    chunked path."""
+    require_gpu()
+    case = synth.prefill_case(f"edge{T}", 90 + T, 8, T, 16, 32, 128, 128, 64, "bf16",
+                              synth.GATE_CHANNEL, 0.01, 0.3, 0.4)
+    announce(f"prefill short/chunked boundary bf16 T={T} B=8 H 16->32 dk=dv=128")
+    o, S = run_prefill(case)
+    o_ref, S_ref = _oracle(case)
+    eo, es = rel(o, o_ref), rel(S, S_ref)
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
 # Long sequences at few (b, h) units: 25 to 61 chunks of 16 (ragged last
 # chunk) and 25 of 64, with a nonzero, a null and an in-place initial state.
 @pytest.mark.parametrize("T,chunk,gate,mode", [

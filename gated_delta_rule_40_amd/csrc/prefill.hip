@@ -9,18 +9,20 @@
 //
 // For a chunk of C tokens entered with state S (dk x dv), with
 // Gamma_r = sum_{s<=r} g_s per key channel:
-//   Kt = K e^Gamma, Kh = K e^-Gamma, Qt = Q e^Gamma, Ke = K e^(Gamma_L - Gamma)
+//   Kt = K e^Gamma, Kh = K e^-Gamma, Qt = Q e^Gamma
 //   A  = strict_lower(diag(beta) Kt Kh^T),   Tb = (I + A)^-1 diag(beta)
 //   P  = lower(Qt Kh^T)
 //   U  = Tb (V - Kt S)                       (the WY pseudo-values minus the
 //                                             pseudo-keys applied to S)
 //   O  = scale (Qt S + P U)
-//   S' = diag(e^Gamma_L) S + Ke^T U
-// which is T token updates regrouped exactly.
+//   S' = diag(e^Gamma_L) (S + Kh^T U)
+// which is T token updates regrouped exactly (the last line is
+// diag(e^Gamma_L) S + (K e^(Gamma_L - Gamma))^T U with the decay factored out,
+// so the chunk needs no third exponential per element).
 //
 // Two kernels:
 //   chunk_prep   one workgroup per (b, h, chunk), all chunks in parallel:
-//                everything that does not depend on S -- Kt, Qt, Ke^T, Tb, P
+//                everything that does not depend on S -- Kt, Qt, Kh^T, Tb, P
 //                and e^Gamma_L -- written to the caller's workspace, one
 //                disjoint block per (b, h, chunk).
 //   chunk_carry  one workgroup per (b, h, slice of DVS state columns), walking
@@ -154,7 +156,7 @@ template <typename OpT, int DK, int C>
 struct ChunkBlock {
   static constexpr int kKt = 0;                  // [C][DK]  K e^Gamma
   static constexpr int kQt = C * DK;             // [C][DK]  Q e^Gamma
-  static constexpr int kKeT = 2 * C * DK;        // [DK][C]  (K e^(Gamma_L - Gamma))^T
+  static constexpr int kKhT = 2 * C * DK;        // [DK][C]  (K e^-Gamma)^T
   static constexpr int kTb = 3 * C * DK;         // [C][C]   (I + A)^-1 diag(beta)
   static constexpr int kP = 3 * C * DK + C * C;  // [C][C]   lower(Qt Kh^T)
   static constexpr int kOpElems = 3 * C * DK + 2 * C * C;
@@ -171,7 +173,7 @@ struct ChunkBlock {
 //   2. row norms through LDS partial sums;
 //   3. per-channel prefix sums (each channel split into row parts, combined
 //      through LDS) and the decayed operands, built in fp32 and rounded once;
-//      Kt, Qt and Ke^T leave for the block from registers;
+//      Kt, Qt and Kh^T leave for the block from registers;
 //   4. A and P on MFMA, computed transposed so that each lane holds four
 //      consecutive columns of a row; P leaves for the block from registers;
 //   5. (I + A)^-1 blocked by 16: the diagonal 16x16 blocks by forward
@@ -399,7 +401,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
   }
 
   // ---- 3. per-channel prefix sums and decayed operands ----
-  // Kt and Kh go to LDS for A and P.  Kt, Qt and Ke^T also go from registers
+  // Kt and Kh go to LDS for A and P.  Kt, Qt and Kh^T also go from registers
   // straight to the block in fragment order; Qt stays in registers until
   // Kt's storage is free.
   OpT* out = reinterpret_cast<OpT*>(blk_bytes);
@@ -425,7 +427,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
       }
     }
     // gam: Gamma just before row rlo; total: Gamma_L, per channel of the quad.
-    OpT ke[4][RPP];
+    OpT khT[4][RPP];
 #pragma unroll
     for (int i = 0; i < RPP; ++i) {
       const int r = rlo + i;
@@ -438,7 +440,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
         kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
         kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
         qtr[i][u] = from_f32<OpT>(qq[i][u] * e_pos);
-        ke[u][i] = from_f32<OpT>(kq[i][u] * __expf(total[u] - gam[u]));
+        khT[u][i] = kh[u];
       }
       store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
       store_vec4<OpT>(Kh_s + r * LDK + 4 * c4, kh);
@@ -446,7 +448,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
       frag_store<OpT, DK, 4>(out + Blk::kQt, r, 4 * c4, qtr[i]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) frag_store<OpT, C, RPP>(out + Blk::kKeT, 4 * c4 + u, rlo, ke[u]);
+    for (int u = 0; u < 4; ++u) frag_store<OpT, C, RPP>(out + Blk::kKhT, 4 * c4 + u, rlo, khT[u]);
     if (part == 0)
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(blk_bytes + Blk::kGammaByte) + 4 * c4) =
           make_float4(expf(total[0]), expf(total[1]), expf(total[2]), expf(total[3]));
@@ -597,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, Chu
 //   [B1]  S^T (operand type) written
 //   c:    R = V - Kt S (to LDS, transposed), O = Qt S (registers)      [B2]
 //   d:    U = Tb R (to LDS, transposed)                                  [B3]
-//   e:    O += P U -> o;  S = e^Gamma_L . S + Ke^T U
+//   e:    O += P U -> o;  S = e^Gamma_L . (S + Kh^T U)
 // ---------------------------------------------------------------------------
 
 
@@ -636,13 +638,13 @@ struct CarryFrags {
   using Sh = CarryShape<OpT, DK, DVS, C>;
   typename Sh::FK::T kt[Sh::OPW][Sh::FK::STEPS], qt[Sh::OPW][Sh::FK::STEPS];
   typename Sh::FC::T tb[Sh::OPW][Sh::FC::STEPS], p[Sh::OPW][Sh::FC::STEPS];
-  typename Sh::FC::T ke[Sh::SPW][Sh::FC::STEPS];
+  typename Sh::FC::T kh[Sh::SPW][Sh::FC::STEPS];
   float v[Sh::OPW][4];
   float gam[Sh::SPW][4];
 };
 
 // Issue the loads of chunk nn's fragments for this wave's tiles, by phase:
-// phase c needs Kt, Qt and V; phase d Tb; phase e P, Ke^T and e^Gamma_L.
+// phase c needs Kt, Qt and V; phase d Tb; phase e P, Kh^T and e^Gamma_L.
 template <typename OpT, int DK, int DVS, int C, int PHASE>
 __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
                                            const unsigned char* ws_head, int nn, int b, int h,
@@ -698,7 +700,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
         const int I = t / Sh::DVT;
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s)
-          F.ke[j][s] = FC::load(blk + Blk::kKeT, 16 * I, s, lane);
+          F.kh[j][s] = FC::load(blk + Blk::kKhT, 16 * I, s, lane);
         const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
         F.gam[j][0] = g4.x;
         F.gam[j][1] = g4.y;
@@ -904,21 +906,21 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
         }
       }
     }
-    // S = diag(e^Gamma_L) S + Ke^T U.
+    // S = diag(e^Gamma_L) (S + Kh^T U).
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = wave * SPW + i;
       if (NST % Sh::NW == 0 || t < NST) {
         const int I = t / DVT, J = t % DVT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[i][e] *= F.gam[i][e];
-        carry_load_gam<OpT, DK, DVS, C>(F, nblk, i, I, lane);
-#pragma unroll
         for (int s = 0; s < FC::STEPS; ++s) {
-          sacc[i] = FC::mma(F.ke[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), sacc[i]);
-          F.ke[i][s] = FC::load(nblk + Blk::kKeT, 16 * I, s, lane);
+          sacc[i] = FC::mma(F.kh[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), sacc[i]);
+          F.kh[i][s] = FC::load(nblk + Blk::kKhT, 16 * I, s, lane);
           pin_order<Sh::kPinLoads>();
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[i][e] *= F.gam[i][e];
+        carry_load_gam<OpT, DK, DVS, C>(F, nblk, i, I, lane);
       }
     }
     // The o rows go out last, after every load of the step.  On gfx9 stores

@@ -256,33 +256,30 @@ __global__ __launch_bounds__((RecShape<DK, DVS>::NT)) void recurrent_kernel(Pref
     }
     if constexpr (kAhead) read_rows(min(t + 1, T - 1));
     __syncthreads();
-    float4 vh4 = red[par][0][0][c4];
+    // Every thread reads both sums (LDS broadcasts); only the store of o is
+    // left to the first row group, so no wave waits on a read of its own.
+    float4 vh4 = red[par][0][0][c4], oh = red[par][1][0][c4];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      const float4 x = red[par][0][w][c4];
+      const float4 x = red[par][0][w][c4], y = red[par][1][w][c4];
       vh4.x += x.x;
       vh4.y += x.y;
       vh4.z += x.z;
       vh4.w += x.w;
+      oh.x += y.x;
+      oh.y += y.y;
+      oh.z += y.z;
+      oh.w += y.w;
     }
-    const float beta = bS[t];
+    const float beta = bS[t], qk = qkS[t];
     const float4 vv = *reinterpret_cast<const float4*>(vS + t * DVS + c4 * 4);
     const float u[4] = {beta * (vv.x - vh4.x), beta * (vv.y - vh4.y), beta * (vv.z - vh4.z),
                         beta * (vv.w - vh4.w)};
+    const float o0 = a.scale * (oh.x + qk * u[0]), o1 = a.scale * (oh.y + qk * u[1]);
+    const float o2 = a.scale * (oh.z + qk * u[2]), o3 = a.scale * (oh.w + qk * u[3]);
     if (tid < C4) {
-      float4 oh = red[par][1][0][c4];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        const float4 x = red[par][1][w][c4];
-        oh.x += x.x;
-        oh.y += x.y;
-        oh.z += x.z;
-        oh.w += x.w;
-      }
-      const float qk = qkS[t];
       IoT* op = og + ((static_cast<size_t>(b) * T + t) * a.H_v + h) * a.dv + j0;
-      store4<IoT>(op, a.scale * (oh.x + qk * u[0]), a.scale * (oh.y + qk * u[1]),
-                  a.scale * (oh.z + qk * u[2]), a.scale * (oh.w + qk * u[3]));
+      store4<IoT>(op, o0, o1, o2, o3);
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {

@@ -81,13 +81,53 @@ def traffic_from_profile(kernel_key: str, digest: str):
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def decode_bytes_per_step(B, H_qk, H_v, dk, dv) -> int:
+def decode_bytes_per_step(B, H_qk, H_v, dk, dv, fused_gate=False) -> int:
     state = 2 * B * H_v * dk * dv * 4
     qkv = B * (2 * H_qk * dk + H_v * dv) * 2
-    gate = B * H_v * dk * 4
+    # channel gate: g [B,H_v,dk]; fused scalar gate: x [B,H_v] plus A_log, dt_bias [H_v]
+    gate = (B * H_v + 2 * H_v) * 4 if fused_gate else B * H_v * dk * 4
     beta = B * H_v * 4
     o = B * H_v * dv * 2
     return state + qkv + gate + beta + o
+
+
+def host_cpu() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_decode_b1_fused(K=256):
+    """The single-sequence fused step: B=1, H_qk=16 -> H_v=32, dk=dv=128, bf16
+    packed q|k|v, scalar decay -exp(A_log) softplus(x + dt_bias), fresh inputs
+    every step, the state carried; K steps captured in a HIP graph and
+    replayed.  At 4.2 MB per step this is a latency figure, not a bandwidth
+    one."""
+    case = synth.fused_decode(seed=2, steps=K)
+    t = case.tensors
+    qkv, x, bl = up(t["qkv"]), up(t["gate_in"]), up(t["beta_logit"])
+    A_log, dt = up(t["A_log"]), up(t["dt_bias"])
+    S0 = up(t["S0"])
+    S = S0.clone()
+    o = torch.empty((1, case.H_v, case.dv), dtype=torch.bfloat16, device=DEV)
+    kw = dict(H_qk=case.H_qk, H_v=case.H_v, dk=case.dk, dv=case.dv, gate=case.gate,
+              A_log=A_log, dt_bias=dt)
+
+    def run():
+        for i in range(K):
+            gdr.gdr_decode_step(qkv[i], x[i], bl[i], S, o, **kw)
+
+    S.copy_(S0)
+    us = graph_us(run, reps=3) / K
+    nbytes = decode_bytes_per_step(1, case.H_qk, case.H_v, case.dk, case.dv, fused_gate=True)
+    return dict(workload="fused_decode_b1: B=1, H_qk=16->H_v=32, dk=dv=128, bf16 packed q|k|v, "
+                         "fused scalar gate, fresh inputs per step",
+                us_per_step=us, gbs=nbytes / us / 1e3, bytes_per_step=nbytes,
+                timing=f"HIP events around graph replays of {K} steps, / steps")
 
 
 def bench_decode(K, W, B):
@@ -221,6 +261,7 @@ def cpu_decode(case, seconds):
     el = time.perf_counter() - t0
     nbytes = decode_bytes_per_step(case.B, case.H_qk, case.H_v, case.dk, case.dv)
     return dict(value=nbytes * steps / el / 1e9, unit="GB/s", cores=thr, kind="oracle",
+                host=host_cpu(),
                 sample=f"{steps} consecutive decode steps of the B={case.B} batch "
                        f"({el:.1f} s, fp64 C recurrence, OpenMP over (b,h))")
 
@@ -412,6 +453,7 @@ def cpu_prefill(case, seconds):
     el = time.perf_counter() - t0
     frac = heads / case.H_v
     return dict(value=case.B * case.T * frac / el, unit="tokens/s", cores=thr, kind="oracle",
+                host=host_cpu(),
                 sample=f"{heads} of {case.H_v} value heads over all {case.T} tokens "
                        f"({el:.1f} s, fp64 token recurrence, OpenMP over heads); "
                        f"tokens/s scaled to all heads")
@@ -458,6 +500,9 @@ def main():
     if "decode" in legs:
         dec = bench_decode(args.steps, args.warmup, args.batch)
         print(f"[bench] decode done: {dec['value']:.1f} GB/s", file=sys.stderr, flush=True)
+        dec["b1_fused"] = bench_decode_b1_fused()
+        print(f"[bench] fused B=1 decode done: {dec['b1_fused']['us_per_step']:.2f} us/step",
+              file=sys.stderr, flush=True)
     pre = None
     if "prefill" in legs:
         pre = bench_prefill(args.prefill_reps, args.prefill_warmup)
@@ -493,6 +538,7 @@ def main():
                        "hbm_peak_frac_of_wall": dec["value"] / HBM_PEAK_GBS},
             "kernel_us_mean": dec["kernel_us_mean"], "graph_event_ms": dec["graph_event_ms"],
             "eager": dec["eager"],
+            "decode_b1_fused": dec["b1_fused"],
             "roofline": dec["roofline"],
             "cpu_baseline": cpu_dec,
         })

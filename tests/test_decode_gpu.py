@@ -114,6 +114,21 @@ def test_decode_batched_channel_b64_256_steps():
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,rows", [(8, [0, 3, 7]), (160, [0, 77, 159])])
+def test_decode_slice_widths_bf16(B, rows):
+    """H_qk 16 -> H_v 32, dk=dv=128, bf16, channel gate, 3 steps: B=8 runs
+    32-column slices; B=160 (a 320 MiB state, beyond the 256 MiB MALL) whole
+    128-column rows, 5120 workgroups.  The oracle follows the sampled batch
+    rows."""
+    case = synth.decode_case(f"slices{B}", 45 + B, B, 3, 16, 32, 128, 128, "bf16",
+                             synth.GATE_CHANNEL, 0.01, 0.5, 0.02)
+    announce(f"decode bf16 B={B} H 16->32 dk=dv=128 steps=3")
+    eo, es = _decode_run(case, 3, rows=rows)
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
 def test_decode_write_then_read_identity():
     """beta = 1 (large logit), q = k: the value just written is read back."""
     case = synth.decode_case("ident", 41, 3, 3, 2, 4, 64, 64, "f32", synth.GATE_CHANNEL,

@@ -20,7 +20,8 @@
 // Thread layout: C4 = DVS/4 lanes cover a row slice as float4s (a wave reads
 // whole 512-byte rows when DVS = 128), RG = NT/C4 row groups each own
 // RPT = dk/RG consecutive rows.  Column sums over rows are reduced first
-// across the row groups inside a wave (lane xor), then across waves in LDS.
+// across the row groups inside a wave (row rotations and lane exchanges), then
+// across waves in LDS.
 #include "device_common.hpp"
 #include "gdr_internal.h"
 #include "gdr.h"
@@ -172,13 +173,10 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
     p2 += ak * s[m].z;
     p3 += ak * s[m].w;
   }
-#pragma unroll
-  for (int off = C4; off < 64; off <<= 1) {
-    p0 += __shfl_xor(p0, off, 64);
-    p1 += __shfl_xor(p1, off, 64);
-    p2 += __shfl_xor(p2, off, 64);
-    p3 += __shfl_xor(p3, off, 64);
-  }
+  p0 = lane_class_sum<C4>(p0);  // over the row groups of the wave
+  p1 = lane_class_sum<C4>(p1);
+  p2 = lane_class_sum<C4>(p2);
+  p3 = lane_class_sum<C4>(p3);
   if (lane < C4) red[0][wave][c4] = make_float4(p0, p1, p2, p3);
   __syncthreads();
   float4 vh4 = red[0][0][c4];
@@ -209,13 +207,10 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
     o2 += qq * t.z;
     o3 += qq * t.w;
   }
-#pragma unroll
-  for (int off = C4; off < 64; off <<= 1) {
-    o0 += __shfl_xor(o0, off, 64);
-    o1 += __shfl_xor(o1, off, 64);
-    o2 += __shfl_xor(o2, off, 64);
-    o3 += __shfl_xor(o3, off, 64);
-  }
+  o0 = lane_class_sum<C4>(o0);  // over the row groups of the wave
+  o1 = lane_class_sum<C4>(o1);
+  o2 = lane_class_sum<C4>(o2);
+  o3 = lane_class_sum<C4>(o3);
   if (lane < C4) red[1][wave][c4] = make_float4(o0, o1, o2, o3);
   __syncthreads();
   if (tid < C4) {

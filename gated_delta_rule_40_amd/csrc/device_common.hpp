@@ -71,12 +71,29 @@ __device__ __forceinline__ void store_vec4(T* __restrict__ p, const T (&v)[4]) {
   }
 }
 
-// Sum over the 64 lanes of a wave; every lane gets the total.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+// Sum of x over the lanes of a wave that share lane % OFF (OFF a power of two
+// below 64); every such lane gets the sum.  Inside each 16-lane row the sum
+// is taken by row rotations (DPP row_ror by OFF, 2 OFF, ... 8: after them a
+// lane holds its row's sum over its residue class), across rows by lane
+// exchanges (xor 16, 32).  A rotation step costs one VALU instruction, a lane
+// exchange a round trip through the LDS crossbar.
+template <int OFF>
+__device__ __forceinline__ float lane_class_sum(float x) {
+  if constexpr (OFF >= 64) {
+    return x;
+  } else {
+    if constexpr (OFF < 16)
+      x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0u, __builtin_bit_cast(unsigned, x), 0x120 + OFF,
+                                         0xf, 0xf, false));  // row_ror:OFF
+    else
+      x += __shfl_xor(x, OFF, 64);
+    return lane_class_sum<2 * OFF>(x);
+  }
 }
+
+// Sum over the 64 lanes of a wave; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float x) { return lane_class_sum<1>(x); }
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
 

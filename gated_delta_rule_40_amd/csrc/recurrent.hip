@@ -60,24 +60,6 @@ struct RecShape {
   static_assert(NT % 64 == 0 && NT <= 256, "workgroup must be whole waves");
 };
 
-// Sum of x over the lanes of a wave that share lane % C4 (the row groups of
-// one column quad), by xor steps OFF, 2 OFF, ... 32: row rotations (DPP)
-// inside each 16-lane row, lane exchanges across rows.
-template <int OFF>
-__device__ __forceinline__ float row_group_sum(float x) {
-  if constexpr (OFF >= 64) {
-    return x;
-  } else {
-    if constexpr (OFF < 16)
-      x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                         0u, __builtin_bit_cast(unsigned, x), 0x120 + OFF,
-                                         0xf, 0xf, false));  // row_ror:OFF
-    else
-      x += __shfl_xor(x, OFF, 64);
-    return row_group_sum<2 * OFF>(x);
-  }
-}
-
 template <typename IoT, int DK, int DVS, bool kChannel>
 __global__ __launch_bounds__((RecShape<DK, DVS>::NT)) void recurrent_kernel(PrefillArgs a) {
   using Sh = RecShape<DK, DVS>;
@@ -246,8 +228,8 @@ __global__ __launch_bounds__((RecShape<DK, DVS>::NT)) void recurrent_kernel(Pref
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      pv[c] = row_group_sum<C4>(pv[c]);
-      po[c] = row_group_sum<C4>(po[c]);
+      pv[c] = lane_class_sum<C4>(pv[c]);
+      po[c] = lane_class_sum<C4>(po[c]);
     }
     const int par = t & 1;
     if (lane < C4) {

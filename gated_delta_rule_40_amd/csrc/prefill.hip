@@ -432,11 +432,28 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
     for (int i = 0; i < RPP; ++i) {
       const int r = rlo + i;
       OpT kt[4], kh[4];
+      float ep[4], en[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) gam[u] += gq[i][u];
+      if constexpr (kChannel) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ep[u] = __expf(gam[u]);
+          en[u] = __expf(-gam[u]);
+        }
+      } else {
+        // One decay per row: the four prefix sums are the same operations on
+        // the same values, so one pair of exponentials serves the quad.
+        const float p = __expf(gam[0]), n = __expf(-gam[0]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ep[u] = p;
+          en[u] = n;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        gam[u] += gq[i][u];
-        const float e_pos = __expf(gam[u]);
-        const float e_neg = __expf(-gam[u]);
+        const float e_pos = ep[u], e_neg = en[u];
         kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
         kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
         qtr[i][u] = from_f32<OpT>(qq[i][u] * e_pos);

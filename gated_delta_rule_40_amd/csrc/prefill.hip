@@ -48,6 +48,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 template <typename T>
 constexpr int pad_of() {
@@ -435,16 +436,20 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
       float ep[4], en[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) gam[u] += gq[i][u];
+      // e^(+-x) as 2^(+-x log2 e): one scaling serves both signs (the same
+      // values as two fast exponentials, since negation is exact).
       if constexpr (kChannel) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          ep[u] = __expf(gam[u]);
-          en[u] = __expf(-gam[u]);
+          const float x = gam[u] * kLog2e;
+          ep[u] = __builtin_amdgcn_exp2f(x);
+          en[u] = __builtin_amdgcn_exp2f(-x);
         }
       } else {
         // One decay per row: the four prefix sums are the same operations on
         // the same values, so one pair of exponentials serves the quad.
-        const float p = __expf(gam[0]), n = __expf(-gam[0]);
+        const float x = gam[0] * kLog2e;
+        const float p = __builtin_amdgcn_exp2f(x), n = __builtin_amdgcn_exp2f(-x);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           ep[u] = p;

@@ -35,14 +35,19 @@ namespace {
 // per-row 64-bit addresses in vector registers.
 typedef unsigned int u32x4_t __attribute__((__vector_size__(16)));
 constexpr int kBufferWord3 = 0x00020000;
+constexpr size_t kMallBytes = size_t{256} << 20;  // MI355X Infinity Cache
 
 __device__ __forceinline__ float4 tile_load(__amdgpu_buffer_rsrc_t r, unsigned voff,
                                             unsigned soff) {
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// kNt: the store carries the non-temporal cache policy (bit 1 of the gfx9
+// buffer cache-policy operand).
+template <bool kNt>
 __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                            float4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, soff,
+                                         kNt ? 2 : 0);
 }
 
 template <int DK, int DVS>
@@ -57,7 +62,13 @@ struct DecodeShape {
 };
 
 // kChannel: per-channel log-decays; otherwise one per (b, h), plain or fused.
-template <typename IoT, int DK, int DVS, bool kChannel>
+// kNtStore: the new state is written with the non-temporal cache policy.
+// While the whole state fits the 256 MiB MALL, plain stores keep it there
+// for the next step; beyond it, write-allocating every line of the new state
+// only evicts what the rest of the step needs, and streaming stores are
+// faster (B=160, 192, 256 at dk=dv=128: 12%, 19%, 18%; B=64 and 128: plain
+// 6% and 2% faster).
+template <typename IoT, int DK, int DVS, bool kChannel, bool kNtStore>
 __global__ __launch_bounds__((DecodeShape<DK, DVS>::NT))
 __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
   using Sh = DecodeShape<DK, DVS>;
@@ -201,7 +212,7 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
     t.y = d * t.y + kk * u1;
     t.z = d * t.z + kk * u2;
     t.w = d * t.w + kk * u3;
-    tile_store(srs, boff, m * rstep, t);
+    tile_store<kNtStore>(srs, boff, m * rstep, t);
     o0 += qq * t.x;
     o1 += qq * t.y;
     o2 += qq * t.z;
@@ -228,16 +239,24 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename IoT, int DK, int DVS>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+template <typename IoT, int DK, int DVS, bool kNtStore>
+hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
   if (a.gate == GDR_GATE_CHANNEL)
-    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, true>), dim3(grid),
+    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, true, kNtStore>), dim3(grid),
                        dim3(DecodeShape<DK, DVS>::NT), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, false>), dim3(grid),
+    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, false, kNtStore>), dim3(grid),
                        dim3(DecodeShape<DK, DVS>::NT), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename IoT, int DK, int DVS>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  const size_t state_bytes =
+      static_cast<size_t>(a.B) * a.H_v * static_cast<size_t>(a.dk) * a.dv * sizeof(float);
+  return state_bytes > kMallBytes ? launch_nt<IoT, DK, DVS, true>(a, stream)
+                                  : launch_nt<IoT, DK, DVS, false>(a, stream);
 }
 
 template <typename IoT, int DK>

@@ -61,6 +61,23 @@ __device__ __forceinline__ void store4(T* __restrict__ p, float a, float b, floa
   }
 }
 
+// store4 with the non-temporal cache policy (the value goes to memory
+// without being kept in the caches).
+typedef unsigned nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ void store4_nt(T* __restrict__ p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 4) {
+    const nt_f32x4 v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<nt_f32x4*>(p));
+  } else {
+    const T e[4] = {from_f32<T>(a), from_f32<T>(b), from_f32<T>(c), from_f32<T>(d)};
+    nt_u32x2 w;
+    __builtin_memcpy(&w, e, sizeof(w));
+    __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x2*>(p));
+  }
+}
+
 // Store 4 io-dtype values held as T (8 or 16 bytes, aligned).
 template <typename T>
 __device__ __forceinline__ void store_vec4(T* __restrict__ p, const T (&v)[4]) {

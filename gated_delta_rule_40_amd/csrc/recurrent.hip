@@ -106,7 +106,7 @@ __global__ __launch_bounds__((RecShape<DK, DVS>::NT)) void recurrent_kernel(Pref
     for (int m = 0; m < RPT; ++m) s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  // ---- pre-pass: every token's head vectors, v slice and beta into LDS ----
+  // ---- pre-pass: every token's head vectors, v slice, beta and q.k into LDS ----
   // Wave w takes tokens w, w + NW, ...; a batch of G of them has all its loads
   // issued before any is used.  Indices past the end are clamped (loaded,
   // then not written).

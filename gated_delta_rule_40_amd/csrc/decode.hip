@@ -106,17 +106,34 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
   float vv[4];
   load_row<IoT, 4>(vh + j0, vv);
   const float beta = sigmoidf(a.beta_logit[bh]);
-  // Every wave reads the whole head's k and q (lanes past dk read element
-  // dk - 1, masked) and keeps them raw until the tile has been requested, so
-  // that nothing waits on them before that.
+  // Every wave reads the whole head's k, q (and channel gate) and keeps them
+  // raw until the tile has been requested, so that nothing waits on them
+  // before that.
+  // kVec (bf16 rows, channel gate): one 16-byte load per lane covers all
+  // three -- lanes 0-15 k, 16-31 q (8 values a lane), 32-63 the gate (4 a
+  // lane) -- so each norm is a sum over one 16-lane row.  Otherwise every
+  // lane reads element lane (+64) of each (lanes past dk read element dk - 1,
+  // masked).
+  constexpr bool kVec = kChannel && sizeof(IoT) == 2 && DK <= 128;
+  constexpr int KL = DK / 8, GL = DK / 4;  // lanes holding k (or q), the gate
+  const int vrow = lane >> 4, vpos = lane & 15;
+  uint4 rv4 = make_uint4(0u, 0u, 0u, 0u);
   IoT rk[NE], rq[NE];
   float eg[NE];
+  if constexpr (kVec) {
+    const void* src;
+    if (vrow == 0) src = kh + 8 * min(vpos, KL - 1);
+    else if (vrow == 1) src = qh + 8 * min(vpos, KL - 1);
+    else src = a.gate_in + bh * DK + 4 * min(lane - 32, GL - 1);
+    rv4 = *static_cast<const uint4*>(src);
+  } else {
 #pragma unroll
-  for (int u = 0; u < NE; ++u) {
-    const int e = min(lane + 64 * u, DK - 1);
-    rk[u] = kh[e];
-    rq[u] = qh[e];
-    if constexpr (kChannel) eg[u] = a.gate_in[bh * DK + e];
+    for (int u = 0; u < NE; ++u) {
+      const int e = min(lane + 64 * u, DK - 1);
+      rk[u] = kh[e];
+      rq[u] = qh[e];
+      if constexpr (kChannel) eg[u] = a.gate_in[bh * DK + e];
+    }
   }
 
   // The state tile (dk x dv fp32, at most 64 KiB) through a buffer descriptor.
@@ -133,7 +150,38 @@ __attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
   // Every wave builds the whole head's vectors and writes them to the same
   // LDS words; the values are identical, and each wave reads only after its
   // own writes, so no barrier is needed before pass 1.
-  {
+  if constexpr (kVec) {
+    if (vrow < 2) {
+      const IoT* e8 = reinterpret_cast<const IoT*>(&rv4);
+      float x[8];
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = to_f32(e8[j]);
+        ss += x[j] * x[j];
+      }
+      ss = row16_sum(vpos < KL ? ss : 0.0f);
+      const float inv = a.l2norm ? 1.0f / sqrtf(ss + kL2Eps) : 1.0f;
+      if (vpos < KL) {
+        float* dst = (vrow == 0 ? kS : qS) + 8 * vpos;
+        *reinterpret_cast<float4*>(dst) = make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+      }
+    } else if (lane - 32 < GL) {
+      const float4 g = *reinterpret_cast<const float4*>(&rv4);
+      *reinterpret_cast<float4*>(dS + 4 * (lane - 32)) =
+          make_float4(expf(g.x), expf(g.y), expf(g.z), expf(g.w));
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): k and the decays are in LDS
+    __builtin_amdgcn_wave_barrier();
+    if (lane < DK / 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(kS + 4 * lane);
+      const float4 d4 = *reinterpret_cast<const float4*>(dS + 4 * lane);
+      *reinterpret_cast<float4*>(akS + 4 * lane) =
+          make_float4(d4.x * k4.x, d4.y * k4.y, d4.z * k4.z, d4.w * k4.w);
+    }
+  } else {
     float ek[NE], eq[NE];
 #pragma unroll
     for (int u = 0; u < NE; ++u) {

@@ -109,6 +109,21 @@ __device__ __forceinline__ float lane_class_sum(float x) {
   }
 }
 
+// Sum over each 16-lane row of a wave (DPP row rotations only); every lane
+// gets its row's total.
+__device__ __forceinline__ float row16_sum(float x) {
+#define GDR_ROR(n)                                                                      \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                           \
+                                     0u, __builtin_bit_cast(unsigned, x), 0x120 + (n), \
+                                     0xf, 0xf, false))
+  GDR_ROR(1);
+  GDR_ROR(2);
+  GDR_ROR(4);
+  GDR_ROR(8);
+#undef GDR_ROR
+  return x;
+}
+
 // Sum over the 64 lanes of a wave; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float x) { return lane_class_sum<1>(x); }
 

@@ -70,7 +70,8 @@ struct DecodeShape {
 // 6% and 2% faster).
 template <typename IoT, int DK, int DVS, bool kChannel, bool kNtStore>
 __global__ __launch_bounds__((DecodeShape<DK, DVS>::NT))
-__attribute__((amdgpu_waves_per_eu(5))) void decode_kernel(DecodeArgs a) {
+__attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void decode_kernel(
+    DecodeArgs a) {
   using Sh = DecodeShape<DK, DVS>;
   constexpr int C4 = Sh::C4, RPT = Sh::RPT, NW = Sh::NW;
   constexpr int NE = (DK + 63) / 64;  // head elements per lane of wave 0

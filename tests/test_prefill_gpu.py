@@ -174,6 +174,26 @@ def test_prefill_short_token_path(T, B, H_qk, H_v, dk, dv, gate, io, mode):
     assert eo < TOL[io] and es < TOL[io]
 
 
+@pytest.mark.timeout(600)
+def test_prefill_short_beyond_cache_b160():
+    """Token-by-token path with a 320 MiB state (B=160, H 16 -> 32,
+    dk=dv=128, bf16, T=4): the final state goes out with streaming stores.
+    The oracle follows sampled (b, h) units."""
+    require_gpu()
+    case = synth.prefill_case("short160", 97, 160, 4, 16, 32, 128, 128, 64, "bf16",
+                              synth.GATE_CHANNEL, 0.01, 0.3, 0.4)
+    announce("prefill short bf16 B=160 T=4 H 16->32 dk=dv=128 (state beyond the MALL)")
+    o, S = run_prefill(case, on_device=True)
+    heads = [(0, 0), (77, 13), (159, 31)]
+    ref = _oracle(case, heads=heads)
+    worst_o = worst_s = 0.0
+    for (b, h), (o_ref, S_ref) in ref.items():
+        worst_o = max(worst_o, rel(to_host(o[b, :, h]), o_ref[0, :, 0]))
+        worst_s = max(worst_s, rel(to_host(S[b, h]), S_ref[0, 0]))
+    print(f"err o={worst_o:.3e} S={worst_s:.3e}")
+    assert worst_o < TOL["bf16"] and worst_s < TOL["bf16"]
+
+
 @pytest.mark.parametrize("T", [24, 25])
 def test_prefill_short_path_boundary(T):
     """B=8, H 16 -> 32, dk=dv=128, bf16, chunk 64: T=24 is the last length on

@@ -921,15 +921,26 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
     }
     __syncthreads();  // [B3]
 
-    // O = scale (Qt S + P U) -> o rows of this chunk.
+    // O = scale (Qt S + P U) -> o rows of this chunk.  When the contractions
+    // over dk and over the chunk use different MFMA shapes (16x16x32 and
+    // 16x16x16), P U goes to accumulators of its own: the compiler may sink the
+    // Qt S product (it touches no memory) next to this one, and it puts no wait
+    // states between an accumulator written by one shape and read as the
+    // addend of the other, which then reads two of its four values too early.
+    constexpr bool kSplitO = FK::KS != FC::KS;
+    f32x4 pacc[OPW];
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
       const int t = wave * OPW + i;
+      pacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (NOT % Sh::NW == 0 || t < NOT) {
         const int R = t / DVT, J = t % DVT;
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s) {
-          oacc[i] = FC::mma(FC::load_pad(Ut_s, LDC, 16 * J, s, lane), F.p[i][s], oacc[i]);
+          if constexpr (kSplitO)
+            pacc[i] = FC::mma(FC::load_pad(Ut_s, LDC, 16 * J, s, lane), F.p[i][s], pacc[i]);
+          else
+            oacc[i] = FC::mma(FC::load_pad(Ut_s, LDC, 16 * J, s, lane), F.p[i][s], oacc[i]);
           F.p[i][s] = FC::load(nblk + Blk::kP, 16 * R, s, lane);
           pin_order<Sh::kPinLoads>();
         }
@@ -967,6 +978,10 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
         const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
         const int r = 16 * R + (lane & 15);
         OpT* op = obase + (static_cast<unsigned>(r) * rs + 16 * J + 4 * (lane >> 4));
+        if constexpr (kSplitO) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[i][e] += pacc[i][e];
+        }
         if (kFull || r < L) {
           if constexpr (Sh::kNtO)
             store4_nt<OpT>(op, a.scale * oacc[i][0], a.scale * oacc[i][1], a.scale * oacc[i][2],

@@ -83,9 +83,10 @@ def test_prefill_head_dims(dk, dv, io):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_prefill_slice_widths(B, io):
     """H 16 -> 32, dk=dv=128 at B=1, 2, 4: the carry splits dv into slices of
-    16, 32 and 64 columns respectively (one workgroup per CU), so every slice
-    width and its fragment schedule is checked against the oracle, with a
-    nonzero initial state and a ragged last chunk."""
+    16, 32 and 64 columns respectively (bf16 at B=1: one wave per 16-column
+    slice; otherwise one workgroup per CU), so every slice width and its
+    fragment schedule is checked against the oracle, with a nonzero initial
+    state and a ragged last chunk."""
     require_gpu()
     case = synth.prefill_case("slices", 300 + B, B, 150, 16, 32, 128, 128, 64, io,
                               synth.GATE_CHANNEL, 0.001, 0.2, 0.02)
@@ -94,6 +95,35 @@ def test_prefill_slice_widths(B, io):
     o_ref, S_ref = _oracle(case)
     print(f"err o={rel(o, o_ref):.3e} S={rel(S, S_ref):.3e}")
     assert rel(o, o_ref) < TOL[io] and rel(S, S_ref) < TOL[io]
+
+
+@pytest.mark.parametrize("B,H_qk,H_v,dk,dv,chunk,T", [
+    # one wave per 16-column slice (B * H_v * dv / 16 <= 256)
+    (2, 2, 4, 32, 32, 16, 77),
+    (2, 2, 4, 16, 32, 64, 77),
+    (2, 2, 4, 64, 16, 16, 77),
+    (2, 2, 4, 16, 64, 32, 77),
+    (1, 1, 2, 128, 16, 16, 77),
+    # one workgroup per slice of 32 columns (288 slices of 16) and of 64 (768)
+    (3, 4, 12, 16, 128, 64, 70),
+    (3, 4, 12, 128, 128, 16, 70),
+    (4, 8, 24, 16, 128, 32, 40),
+])
+def test_prefill_mixed_mfma_shapes(B, H_qk, H_v, dk, dv, chunk, T):
+    """bf16 shapes whose two contractions use different MFMA forms (16x16x32
+    over a 32-multiple, 16x16x16 over 16): dk = 16 with chunk 32 or 64, or
+    chunk 16 with dk >= 32.  The output sums a product of each form, so these
+    cases check that neither carry accumulates one form into an accumulator
+    the other is still writing.  The last three take the workgroup carry at
+    the shapes whose compiled code had put the two products closest together."""
+    require_gpu()
+    case = synth.prefill_case("mixed", 400 + dk + chunk, B, T, H_qk, H_v, dk, dv, chunk, "bf16",
+                              synth.GATE_CHANNEL, 0.01, 0.3, 0.3)
+    announce(f"prefill mixed MFMA forms B={B} T={T} H {H_qk}->{H_v} dk={dk} dv={dv} chunk={chunk}")
+    o, S = run_prefill(case)
+    o_ref, S_ref = _oracle(case)
+    print(f"err o={rel(o, o_ref):.3e} S={rel(S, S_ref):.3e}")
+    assert rel(o, o_ref) < TOL["bf16"] and rel(S, S_ref) < TOL["bf16"]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])

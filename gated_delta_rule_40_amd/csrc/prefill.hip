@@ -173,10 +173,13 @@ struct ChunkBlock {
 //      quads of k, q, g over a part of the rows; beta once per row);
 //   2. row norms through LDS partial sums;
 //   3. per-channel prefix sums (each channel split into row parts, combined
-//      through LDS) and the decayed operands, built in fp32 and rounded once;
-//      Kt, Qt and Kh^T leave for the block from registers;
+//      through LDS) and the decayed operands, built in fp32 and rounded once
+//      into row-major LDS;
 //   4. A and P on MFMA, computed transposed so that each lane holds four
 //      consecutive columns of a row; P leaves for the block from registers;
+//      Kt, Qt and Kh^T are copied from LDS to the block while their LDS
+//      regions are still live, consecutive threads writing consecutive lane
+//      slices (Kh^T read down the columns of Kh);
 //   5. (I + A)^-1 blocked by 16: the diagonal 16x16 blocks by forward
 //      substitution in registers (one lane per column), then the off-diagonal
 //      blocks level by level, T_ij = -T_ii sum_k A_ik T_kj, with fp32 MFMA;
@@ -253,6 +256,48 @@ __device__ __forceinline__ void frag_store(OpT* region, int row, int col0, const
     W w;
     __builtin_memcpy(&w, &v[j * G], kB);
     *reinterpret_cast<W*>(region + frag_off<OpT, KD>(row, col0 + j * G)) = w;
+  }
+}
+
+// Copy a ROWS x KD region held row-major in LDS (row pitch ld, rows 16-byte
+// aligned) to a block region in fragment order.  Thread t writes slots t,
+// t + kThreads, ...: consecutive lanes write consecutive lane slices, so each
+// wave store covers one contiguous run of 64 slices (1 KiB in bf16) instead of
+// pieces scattered over the fragment layout.
+template <typename OpT, int KD, int ROWS>
+__device__ __forceinline__ void lds_to_frag(OpT* region, const OpT* src, int ld, int tid) {
+  using F = FragT<OpT, KD>;
+  using V = typename F::T;
+  constexpr int N = ROWS * KD / F::VL;  // slots
+#pragma unroll
+  for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i) {
+    const int d = tid + i * kThreads;
+    if (N % kThreads == 0 || d < N) {
+      const V v = *reinterpret_cast<const V*>(src + F::slot_row(d) * ld + F::slot_col(d));
+      *reinterpret_cast<V*>(region + d * F::VL) = v;
+    }
+  }
+}
+
+// The same for the transpose of a row-major LDS buffer: region row r (of
+// ROWS), column c (of KD) is src[c * ld + r].
+template <typename OpT, int KD, int ROWS>
+__device__ __forceinline__ void lds_to_frag_t(OpT* region, const OpT* src, int ld, int tid) {
+  using F = FragT<OpT, KD>;
+  using V = typename F::T;
+  constexpr int N = ROWS * KD / F::VL;  // slots
+#pragma unroll
+  for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i) {
+    const int d = tid + i * kThreads;
+    if (N % kThreads == 0 || d < N) {
+      const int r = F::slot_row(d), c = F::slot_col(d);
+      OpT v[F::VL];
+#pragma unroll
+      for (int j = 0; j < F::VL; ++j) v[j] = src[(c + j) * ld + r];
+      V w;
+      __builtin_memcpy(&w, v, sizeof(V));
+      *reinterpret_cast<V*>(region + d * F::VL) = w;
+    }
   }
 }
 
@@ -428,7 +473,6 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
       }
     }
     // gam: Gamma just before row rlo; total: Gamma_L, per channel of the quad.
-    OpT khT[4][RPP];
 #pragma unroll
     for (int i = 0; i < RPP; ++i) {
       const int r = rlo + i;
@@ -462,15 +506,10 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
         kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
         kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
         qtr[i][u] = from_f32<OpT>(qq[i][u] * e_pos);
-        khT[u][i] = kh[u];
       }
       store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
       store_vec4<OpT>(Kh_s + r * LDK + 4 * c4, kh);
-      frag_store<OpT, DK, 4>(out + Blk::kKt, r, 4 * c4, kt);
-      frag_store<OpT, DK, 4>(out + Blk::kQt, r, 4 * c4, qtr[i]);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) frag_store<OpT, C, RPP>(out + Blk::kKhT, 4 * c4 + u, rlo, khT[u]);
     if (part == 0)
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(blk_bytes + Blk::kGammaByte) + 4 * c4) =
           make_float4(expf(total[0]), expf(total[1]), expf(total[2]), expf(total[3]));
@@ -495,6 +534,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
         make_float4(row > col ? br * acc[0] : 0.0f, row > col + 1 ? br * acc[1] : 0.0f,
                     row > col + 2 ? br * acc[2] : 0.0f, row > col + 3 ? br * acc[3] : 0.0f);
   }
+  lds_to_frag<OpT, DK, C>(out + Blk::kKt, Kt_s, LDK, tid);
   __syncthreads();  // Kt is dead: its storage takes Qt
   if (active) {
 #pragma unroll
@@ -515,6 +555,8 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
     for (int e = 0; e < 4; ++e) v[e] = from_f32<OpT>(row >= col + e ? acc[e] : 0.0f);
     frag_store<OpT, C, 4>(out + Blk::kP, row, col, v);
   }
+  lds_to_frag<OpT, DK, C>(out + Blk::kQt, Qt_s, LDK, tid);
+  lds_to_frag_t<OpT, C, DK>(out + Blk::kKhT, Kh_s, LDK, tid);
   __syncthreads();  // Kh and Qt are dead: their storage takes T and the solve scratch
 
   // ---- 5a. diagonal 16x16 blocks of (I + A)^-1: lane = column ----

@@ -288,15 +288,30 @@ __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void
   }
 }
 
+// Occupancy cap for large grids of whole 128 x 128 tiles with a channel gate,
+// written with plain stores: LDS the kernel does not use, so that at most
+// three workgroups share a CU (160 KiB of LDS over more than 40 KiB each).
+// Fewer tiles in flight contend less for the memory system there (graph
+// replay, bf16: B=64 41.5 -> 41.1 us, B=128 80.7 -> 78.8 us).  Smaller grids
+// lose by it (B=16: 9.5 -> 10.9 us), with streaming stores (B=256) it is
+// neutral, and with a scalar gate (one decay per tile, lighter loads) it costs
+// 0.4-0.9%.
+constexpr unsigned kOccupancyPadBytes = 40 * 1024;
+constexpr unsigned kOccupancyPadMinGrid = 2048;
+
 template <typename IoT, int DK, int DVS, bool kNtStore>
 hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
+  const unsigned pad = (DK == 128 && DVS == 128 && !kNtStore && a.gate == GDR_GATE_CHANNEL &&
+                        grid >= kOccupancyPadMinGrid)
+                           ? kOccupancyPadBytes
+                           : 0;
   if (a.gate == GDR_GATE_CHANNEL)
     hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, true, kNtStore>), dim3(grid),
-                       dim3(DecodeShape<DK, DVS>::NT), 0, stream, a);
+                       dim3(DecodeShape<DK, DVS>::NT), pad, stream, a);
   else
     hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, false, kNtStore>), dim3(grid),
-                       dim3(DecodeShape<DK, DVS>::NT), 0, stream, a);
+                       dim3(DecodeShape<DK, DVS>::NT), pad, stream, a);
   return hipGetLastError();
 }
 

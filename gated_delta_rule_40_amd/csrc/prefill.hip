@@ -704,6 +704,15 @@ struct CarryShape {
   static constexpr bool kNtO = DVS == 16;
 };
 
+// What a carry workgroup computes over its chunk range:
+//   kCarryFull  the o rows and the final state, from the given start state;
+//   kCarryMapN  the final state only, from a zero start state: the constant
+//               part N of the range's affine map S_out = M S_in + N;
+//   kCarryMapM  the final state only, from the identity (dk columns) with
+//               V = 0: the linear part M.  Neither map reads Qt or P or
+//               writes o.
+enum CarryMode { kCarryFull = 0, kCarryMapN = 1, kCarryMapM = 2 };
+
 template <typename OpT, int DK, int DVS, int C>
 struct CarryFrags {
   using Sh = CarryShape<OpT, DK, DVS, C>;
@@ -716,7 +725,7 @@ struct CarryFrags {
 
 // Issue the loads of chunk nn's fragments for this wave's tiles, by phase:
 // phase c needs Kt, Qt and V; phase d Tb; phase e P, Kh^T and e^Gamma_L.
-template <typename OpT, int DK, int DVS, int C, int PHASE>
+template <typename OpT, int DK, int DVS, int C, int PHASE, int MODE>
 __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
                                            const unsigned char* ws_head, int nn, int b, int h,
                                            int jb, int wave, int lane) {
@@ -737,17 +746,22 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
 #pragma unroll
         for (int s = 0; s < FK::STEPS; ++s) {
           F.kt[i][s] = FK::load(blk + Blk::kKt, 16 * R, s, lane);
-          F.qt[i][s] = FK::load(blk + Blk::kQt, 16 * R, s, lane);
+          if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(blk + Blk::kQt, 16 * R, s, lane);
         }
-        // Uniform row base plus 32-bit lane offsets; rows past the end re-read
-        // the last row and are zeroed when used.
-        const OpT* vrow = vg + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
-        const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
-        const int last = a.T - 1 - t0;
+        if constexpr (MODE != kCarryMapM) {
+          // Uniform row base plus 32-bit lane offsets; rows past the end
+          // re-read the last row and are zeroed when used.
+          const OpT* vrow = vg + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
+          const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
+          const int last = a.T - 1 - t0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = min(16 * R + 4 * (lane >> 4) + e, last);
-          F.v[i][e] = to_f32(vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = min(16 * R + 4 * (lane >> 4) + e, last);
+            F.v[i][e] = to_f32(vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) F.v[i][e] = 0.0f;
         }
       }
       if constexpr (PHASE == 1) {
@@ -755,7 +769,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
         for (int s = 0; s < FC::STEPS; ++s)
           F.tb[i][s] = FC::load(blk + Blk::kTb, 16 * R, s, lane);
       }
-      if constexpr (PHASE == 2) {
+      if constexpr (PHASE == 2 && MODE == kCarryFull) {
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s)
           F.p[i][s] = FC::load(blk + Blk::kP, 16 * R, s, lane);
@@ -815,21 +829,23 @@ __device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C>& F, c
   F.gam[i][3] = g4.w;
 }
 
-template <typename OpT, int DK, int DVS, int C>
+template <typename OpT, int DK, int DVS, int C, int MODE>
 __device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C>& F,
                                                const PrefillArgs& a, const unsigned char* ws_head,
                                                int nn, int b, int h, int jb, int wave, int lane) {
-  carry_load<OpT, DK, DVS, C, 0>(F, a, ws_head, nn, b, h, jb, wave, lane);
-  carry_load<OpT, DK, DVS, C, 1>(F, a, ws_head, nn, b, h, jb, wave, lane);
-  carry_load<OpT, DK, DVS, C, 2>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, 0, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, 1, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, 2, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
 }
 
 // One workgroup per (b, h, slice), over the chunks of cr: the state slice
-// starts from s_src (zeros when it is null) and ends in state_out.  wg is the
-// workgroup's index among the G that do this work, and sm its LDS (kSmem bytes).
-template <typename OpT, int DK, int DVS, int C>
+// starts from s_src (zeros when it is null; the identity for kCarryMapM) and ends
+// in s_dst (not written when it is null).  a.dv is the number of state
+// columns (dk for kCarryMapM).  wg is the workgroup's index among the G that do
+// this work, and sm its LDS (kSmem bytes).
+template <typename OpT, int DK, int DVS, int C, int MODE>
 __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
-                                           const float* s_src, int wg, int G,
+                                           const float* s_src, float* s_dst, int wg, int G,
                                            unsigned char* sm) {
   using Sh = CarryShape<OpT, DK, DVS, C>;
   using Blk = typename Sh::Blk;
@@ -871,7 +887,12 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
   for (int i = 0; i < SPW; ++i) {
     const int t = wave * SPW + i;
     sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if ((NST % Sh::NW == 0 || t < NST) && s_src) {
+    if constexpr (MODE == kCarryMapM) {
+      const int I = t / DVT, J = t % DVT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sacc[i][e] = 16 * I + 4 * (lane >> 4) + e == jb + 16 * J + (lane & 15) ? 1.0f : 0.0f;
+    } else if ((NST % Sh::NW == 0 || t < NST) && s_src) {
       const int I = t / DVT, J = t % DVT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -925,11 +946,11 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
           ks = FK::mma(F.kt[i][s], z[s], ks);
           // O is accumulated transposed (S^T Qt^T): each lane then holds four
           // consecutive columns of one output row, stored with one wide write.
-          oacc[i] = FK::mma(z[s], F.qt[i][s], oacc[i]);
+          if constexpr (MODE == kCarryFull) oacc[i] = FK::mma(z[s], F.qt[i][s], oacc[i]);
           // The next chunk's fragments go out one pair per step, each as soon
           // as its registers have been read.
           F.kt[i][s] = FK::load(nblk + Blk::kKt, 16 * R, s, lane);
-          F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
+          if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
           pin_order<Sh::kPinLoads>();
         }
         float rv[4];
@@ -939,7 +960,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
           rv[e] = (r < L ? F.v[i][e] : 0.0f) - ks[e];
         }
         store_tile_t<OpT>(Rt_s, LDC, 16 * J, 16 * R, rv, lane);
-        carry_load_v<OpT, DK, DVS, C>(F, a, nx, b, h, jb, i, R, J, lane);
+        if constexpr (MODE != kCarryMapM) carry_load_v<OpT, DK, DVS, C>(F, a, nx, b, h, jb, i, R, J, lane);
       }
     }
     __syncthreads();  // [B2]
@@ -975,7 +996,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
     for (int i = 0; i < OPW; ++i) {
       const int t = wave * OPW + i;
       pacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (NOT % Sh::NW == 0 || t < NOT) {
+      if (MODE == kCarryFull && (NOT % Sh::NW == 0 || t < NOT)) {
         const int R = t / DVT, J = t % DVT;
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s) {
@@ -1013,7 +1034,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
       const int t = wave * OPW + i;
-      if (NOT % Sh::NW == 0 || t < NOT) {
+      if (MODE == kCarryFull && (NOT % Sh::NW == 0 || t < NOT)) {
         const int R = t / DVT, J = t % DVT;
         // lane (c, g): row 16 R + c, columns 16 J + 4 g ... + 3 of the chunk's o
         OpT* obase = og + ((static_cast<size_t>(b) * a.T + t0) * a.H_v + h) * a.dv + jb;
@@ -1037,13 +1058,14 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
   };
 
   Frags F;
-  carry_load_all<OpT, DK, DVS, C>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
+  carry_load_all<OpT, DK, DVS, C, MODE>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
   const int NF = a.T / C;  // full chunks
   const int nf_end = min(cr.n1, NF);
   for (int nn = cr.n0; nn < nf_end; ++nn) compute(F, nn, std::true_type{});
   if (cr.n1 > NF) compute(F, NF, std::false_type{});  // the ragged last chunk
 
   // ---- final state ----
+  if (!s_dst) return;
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     const int t = wave * SPW + i;
@@ -1052,20 +1074,182 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * I + 4 * (lane >> 4) + e;
-        a.state_out[st_off + static_cast<size_t>(row) * a.dv + jb + 16 * J + (lane & 15)] =
-            sacc[i][e];
+        s_dst[st_off + static_cast<size_t>(row) * a.dv + jb + 16 * J + (lane & 15)] = sacc[i][e];
       }
     }
   }
 }
 
-template <typename OpT, int DK, int DVS, int C>
+// A carry launch runs up to three jobs side by side, each over nseg
+// consecutive sequence segments of seg_len chunks (the last segment of the
+// sequence may be shorter).  Workgroups are job-major, then segment-major.
+struct CarryJob {
+  int mode;           // CarryMode
+  int first, nseg;    // segments first ... first + nseg - 1
+  int per;            // workgroups per segment: (b, h) units x column slices
+  int cols;           // state columns: dv, or dk for kCarryMapM
+  const float* src;   // start state of segment first + i at src + i * src_stride (null: zeros)
+  size_t src_stride;
+  float* dst;         // final state of segment first + i at dst + i * dst_stride (null: none)
+  size_t dst_stride;
+};
+struct CarryJobs {
+  CarryJob job[3];
+  int n;
+  int seg_len;
+};
+
+// kMaps: the launch may hold kCarryMapN / kCarryMapM jobs (instantiated for the one
+// slice width the segmented schedule uses); otherwise every job is kCarryFull.
+template <typename OpT, int DK, int DVS, int C, bool kMaps>
 __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry_kernel(
-    PrefillArgs a, ChunkRange cr, const float* s_src) {
+    PrefillArgs a, CarryJobs J) {
   __shared__ __attribute__((aligned(16))) unsigned char sm[CarryShape<OpT, DK, DVS, C>::kSmem];
-  carry_body<OpT, DK, DVS, C>(a, cr, s_src, blockIdx.x, gridDim.x, sm);
+  int w = blockIdx.x, k = 0;
+  while (k + 1 < J.n && w >= J.job[k].nseg * J.job[k].per) {
+    w -= J.job[k].nseg * J.job[k].per;
+    ++k;
+  }
+  const CarryJob& jb = J.job[k];
+  const int i = w / jb.per;
+  const int p = jb.first + i;
+  const int NC = (a.T + C - 1) / C;
+  const ChunkRange cr{p * J.seg_len, min((p + 1) * J.seg_len, NC)};
+  PrefillArgs ap = a;
+  ap.dv = jb.cols;
+  const float* src = jb.src ? jb.src + i * jb.src_stride : nullptr;
+  float* dst = jb.dst ? jb.dst + i * jb.dst_stride : nullptr;
+  if constexpr (kMaps) {
+    if (jb.mode == kCarryMapN) {
+      carry_body<OpT, DK, DVS, C, kCarryMapN>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+      return;
+    }
+    if (jb.mode == kCarryMapM) {
+      carry_body<OpT, DK, DVS, C, kCarryMapM>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+      return;
+    }
+  }
+  carry_body<OpT, DK, DVS, C, kCarryFull>(ap, cr, src, dst, w % jb.per, jb.per, sm);
 }
 
+// Start states of segments p0 + 1 ... p1 + 1 of the segmented carry:
+// S[p + 1] = M[p] S[p] + N[p] per (b, h) unit, in fp32.  S and N are
+// [segment][unit][DK][dv], M is [segment][unit][DK][DK].  One workgroup per
+// unit and 16-column block; the product runs on fp32 MFMA (16x16x4), wave w
+// owning row tiles TPW w ... TPW w + TPW - 1.  Lane (g, n) holds row
+// 16 I + n of M at k = g KG ... g KG + KG - 1 in registers, so k-step t
+// contracts k = g KG + t over the four lane groups, and S[k][n] comes from
+// LDS (double buffered across segments).  The next segment's M rows and N
+// are loaded while the current product runs.
+template <int DK>
+__global__ __launch_bounds__(256) void carry_scan_kernel(const float* __restrict__ M,
+                                                         const float* __restrict__ N,
+                                                         float* __restrict__ S, int units, int dv,
+                                                         int p0, int p1) {
+  constexpr int NI = DK / 16;          // row tiles
+  constexpr int TPW = (NI + 3) / 4;    // row tiles per wave
+  constexpr int KG = DK / 4;           // k-values per lane group
+  constexpr bool kAllWaves = NI % 4 == 0;  // every wave owns TPW row tiles
+  __shared__ float Ss[2][DK][16];
+  const int nb = dv / 16;
+  const int u = blockIdx.x / nb;
+  const int c0 = (blockIdx.x % nb) * 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const size_t sv = static_cast<size_t>(units) * DK * dv;  // segment stride of S and N
+  const size_t sm = static_cast<size_t>(units) * DK * DK;  // segment stride of M
+  const size_t uv = static_cast<size_t>(u) * DK * dv;
+  const size_t um = static_cast<size_t>(u) * DK * DK;
+
+  static_assert(DK * 16 % 256 == 0, "start state: whole passes of the workgroup");
+  {
+    float s0[DK * 16 / 256];  // every load issued before any is used
+#pragma unroll
+    for (int i = 0; i < DK * 16 / 256; ++i) {
+      const int x = threadIdx.x + 256 * i;
+      s0[i] = S[p0 * sv + uv + static_cast<size_t>(x / 16) * dv + c0 + x % 16];
+    }
+#pragma unroll
+    for (int i = 0; i < DK * 16 / 256; ++i) {
+      const int x = threadIdx.x + 256 * i;
+      Ss[0][x / 16][x % 16] = s0[i];
+    }
+  }
+
+  // Two register sets: segment p + 1's M rows and N are in flight while
+  // segment p's product runs.  Fetches are unconditional (the last segment is
+  // fetched again, unused) so that the wait counts stay exact.
+  float m[2][TPW][KG];
+  float na[2][TPW][4];
+  auto fetch = [&](int p, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      const int I = wave * TPW + ti;
+      if (kAllWaves || I < NI) {
+        const float* mr = M + p * sm + um + static_cast<size_t>(16 * I + n) * DK + g * KG;
+#pragma unroll
+        for (int k4 = 0; k4 < KG / 4; ++k4) {
+          const float4 v = *reinterpret_cast<const float4*>(mr + 4 * k4);
+          m[B][ti][4 * k4] = v.x;
+          m[B][ti][4 * k4 + 1] = v.y;
+          m[B][ti][4 * k4 + 2] = v.z;
+          m[B][ti][4 * k4 + 3] = v.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          na[B][ti][e] = N[p * sv + uv + static_cast<size_t>(16 * I + 4 * g + e) * dv + c0 + n];
+      }
+    }
+  };
+  int cur = 0;
+  auto step = [&](int p, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti)
+      acc[ti] = f32x4{na[B][ti][0], na[B][ti][1], na[B][ti][2], na[B][ti][3]};
+    float bv[KG];  // this lane group's k-values of column n, all read before the products
+#pragma unroll
+    for (int t = 0; t < KG; ++t) bv[t] = Ss[cur][g * KG + t][n];
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      if (kAllWaves || wave * TPW + ti < NI) {
+#pragma unroll
+        for (int t = 0; t < KG; ++t) acc[ti] = mfma_f32x4(m[B][ti][t], bv[t], acc[ti]);
+      }
+    }
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      const int I = wave * TPW + ti;
+      if (kAllWaves || I < NI) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * I + 4 * g + e;
+          Ss[cur ^ 1][row][n] = acc[ti][e];
+          S[(p + 1) * sv + uv + static_cast<size_t>(row) * dv + c0 + n] = acc[ti][e];
+        }
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  };
+  fetch(p0, std::integral_constant<int, 0>{});
+  __syncthreads();
+  // Segments in pairs, each fetch one product ahead of its use; the
+  // scheduling fences keep every fetch ahead of the product it overlaps.
+  int p = p0;
+  for (; p + 1 <= p1; p += 2) {
+    fetch(p + 1, std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    step(p, std::integral_constant<int, 0>{});
+    fetch(min(p + 2, p1), std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    step(p + 1, std::integral_constant<int, 1>{});
+  }
+  if (p <= p1) step(p, std::integral_constant<int, 0>{});  // an odd last segment
+}
 
 // T = 0: state_out = state_in (or zeros).
 __global__ void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
@@ -1095,13 +1279,23 @@ size_t block_bytes_rt(int dk, int chunk) {
   return 0;
 }
 
-template <typename OpT, int DK, int DVS, int C>
-hipError_t launch_carry(const PrefillArgs& a, ChunkRange cr, const float* s_src,
-                        hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
-  hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C>), dim3(grid),
-                     dim3(CarryShape<OpT, DK, DVS, C>::NT), 0, stream, a, cr, s_src);
+template <typename OpT, int DK, int DVS, int C, bool kMaps>
+hipError_t launch_carry_jobs(const PrefillArgs& a, const CarryJobs& J, hipStream_t stream) {
+  unsigned grid = 0;
+  for (int k = 0; k < J.n; ++k) grid += static_cast<unsigned>(J.job[k].nseg) * J.job[k].per;
+  hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, kMaps>), dim3(grid),
+                     dim3(CarryShape<OpT, DK, DVS, C>::NT), 0, stream, a, J);
   return hipGetLastError();
+}
+
+// The plain carry: one job, the whole sequence as one segment.
+template <typename OpT, int DK, int DVS, int C>
+hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
+  CarryJobs J{};
+  J.n = 1;
+  J.seg_len = (a.T + C - 1) / C;
+  J.job[0] = CarryJob{kCarryFull, 0, 1, a.B * a.H_v * (a.dv / DVS), a.dv, a.state_in, 0, a.state_out, 0};
+  return launch_carry_jobs<OpT, DK, DVS, C, false>(a, J, stream);
 }
 
 // Slice width: the narrowest (from 16 columns) that keeps the number of
@@ -1118,13 +1312,106 @@ int carry_slice_width(const PrefillArgs& a) {
 }
 
 template <typename OpT, int DK, int C>
-hipError_t launch_carry_any(const PrefillArgs& a, ChunkRange cr, const float* s_src,
-                            hipStream_t stream) {
+hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
   switch (carry_slice_width(a)) {
-    case 16: return launch_carry<OpT, DK, 16, C>(a, cr, s_src, stream);
-    case 32: return launch_carry<OpT, DK, 32, C>(a, cr, s_src, stream);
-    default: return launch_carry<OpT, DK, 64, C>(a, cr, s_src, stream);
+    case 16: return launch_carry<OpT, DK, 16, C>(a, stream);
+    case 32: return launch_carry<OpT, DK, 32, C>(a, stream);
+    default: return launch_carry<OpT, DK, 64, C>(a, stream);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Segmented carry: a parallel scan of the carry's affine maps.
+//
+// Over a range of chunks the carry maps each state column affinely,
+// S_out = M S_in + N: N is the range run from a zero state, M (dk x dk) the
+// range run from the identity with V = 0.  When the plain carry would leave
+// most CUs idle (few (b, h) units) and the sequence is long, it is cut into P
+// segments of seg_len chunks and run in three launches:
+//   1. segment 0 in full, side by side with the maps (N, M) of segments
+//      1 ... P-2 (the last segment's map is never needed);
+//   2. the start states S_2 ... S_{P-1} by S_{p+1} = M_p S_p + N_p, with S_1
+//      the final state of segment 0 (fp32, a few small products per unit);
+//   3. segments 1 ... P-1 in full from their start states, side by side; the
+//      last one's final state is the result.
+// That is about three times the carry's work for segments 1 ... P-2, spread
+// over P times more workgroups, and two segment lengths of chained steps
+// instead of P.  The maps use the same bf16 (or fp32) operands as the plain
+// carry, so the result matches it to rounding.
+// ---------------------------------------------------------------------------
+constexpr long kSegMaxPlainWgs = 64;  // plain carry workgroups (16-column slices) at most
+constexpr int kSegMinChunks = 8;      // chunks per segment at least
+constexpr int kSegMaxSegments = 16;
+constexpr long kSegMaxWgs = 512;      // workgroups of the side-by-side launch at most
+
+struct SegPlan {
+  int P;        // segments (1: the plain carry)
+  int seg_len;  // chunks per segment
+};
+
+SegPlan carry_segments(int B, int T, int H_v, int dk, int dv, int chunk) {
+  const int NC = (T + chunk - 1) / chunk;
+  const SegPlan plain{1, NC};
+  const long units = static_cast<long>(B) * H_v;
+  const long w_n = units * (dv / 16);  // workgroups per segment of a dv-column job
+  const long w_m = units * (dk / 16);  // of a dk-column (linear part) job
+  if (dv < 16 || dk < 16 || w_n > kSegMaxPlainWgs) return plain;
+  SegPlan best = plain;
+  for (int P = 3; P <= kSegMaxSegments; ++P) {
+    const int L = (NC + P - 1) / P;
+    if (L < kSegMinChunks) break;
+    const int Pe = (NC + L - 1) / L;  // segments actually formed
+    if (Pe < 3) continue;
+    if (w_n + (Pe - 2) * (w_n + w_m) > kSegMaxWgs) break;
+    best = SegPlan{Pe, L};
+  }
+  return best;
+}
+
+// Bytes of the segmented carry's buffers (S and N: [P][units][dk][dv],
+// M: [P][units][dk][dk], fp32), placed after the chunk blocks.
+size_t seg_bytes(SegPlan sp, long units, int dk, int dv) {
+  if (sp.P < 3) return 0;
+  return static_cast<size_t>(sp.P) * units * dk * (2 * static_cast<size_t>(dv) + dk) *
+         sizeof(float);
+}
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+template <typename OpT, int DK, int C>
+hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t stream) {
+  const long units = static_cast<long>(a.B) * a.H_v;
+  const int NC = (a.T + C - 1) / C;
+  const int P = sp.P;
+  const size_t sv = static_cast<size_t>(units) * DK * a.dv;  // one segment's S or N
+  const size_t smm = static_cast<size_t>(units) * DK * DK;   // one segment's M
+  float* Sb = reinterpret_cast<float*>(
+      static_cast<unsigned char*>(a.ws) +
+      align256(static_cast<size_t>(units) * NC * ChunkBlock<OpT, DK, C>::kBytes));
+  float* Nb = Sb + P * sv;
+  float* Mb = Nb + P * sv;
+  const int per_n = static_cast<int>(units) * (a.dv / 16);
+  const int per_m = static_cast<int>(units) * (DK / 16);
+
+  CarryJobs J{};
+  J.n = 3;
+  J.seg_len = sp.seg_len;
+  J.job[0] = CarryJob{kCarryFull, 0, 1, per_n, a.dv, a.state_in, 0, Sb + sv, 0};
+  J.job[1] = CarryJob{kCarryMapN, 1, P - 2, per_n, a.dv, nullptr, 0, Nb + sv, sv};
+  J.job[2] = CarryJob{kCarryMapM, 1, P - 2, per_m, DK, nullptr, 0, Mb + smm, smm};
+  hipError_t err = launch_carry_jobs<OpT, DK, 16, C, true>(a, J, stream);
+  if (err != hipSuccess) return err;
+
+  hipLaunchKernelGGL(carry_scan_kernel<DK>, dim3(static_cast<unsigned>(per_n)), dim3(256), 0,
+                     stream, Mb, Nb, Sb, static_cast<int>(units), a.dv, 1, P - 2);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  CarryJobs R{};
+  R.n = 2;
+  R.seg_len = sp.seg_len;
+  R.job[0] = CarryJob{kCarryFull, 1, P - 2, per_n, a.dv, Sb + sv, sv, nullptr, 0};
+  R.job[1] = CarryJob{kCarryFull, P - 1, 1, per_n, a.dv, Sb + (P - 1) * sv, 0, a.state_out, 0};
+  return launch_carry_jobs<OpT, DK, 16, C, false>(a, R, stream);
 }
 
 template <typename OpT, int DK, int C>
@@ -1144,7 +1431,9 @@ hipError_t launch_dk_c(const PrefillArgs& a, hipStream_t stream) {
   const ChunkRange all{0, (a.T + C - 1) / C};
   const hipError_t err = launch_prep<OpT, DK, C>(a, all, stream);
   if (err != hipSuccess) return err;
-  return launch_carry_any<OpT, DK, C>(a, all, a.state_in, stream);
+  const SegPlan sp = carry_segments(a.B, a.T, a.H_v, DK, a.dv, C);
+  if (sp.P >= 3) return launch_carry_segmented<OpT, DK, C>(a, sp, stream);
+  return launch_carry_any<OpT, DK, C>(a, stream);
 }
 
 template <typename OpT, int DK>
@@ -1171,11 +1460,13 @@ hipError_t launch_io(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int B, int T, int H_v, int dk, int dv, int chunk, int io_bf16) {
-  (void)dv;
   if (B <= 0 || T <= 0) return 0;
   const size_t nc = (static_cast<size_t>(T) + chunk - 1) / chunk;
   const size_t bb = io_bf16 ? block_bytes_rt<bf16>(dk, chunk) : block_bytes_rt<float>(dk, chunk);
-  return static_cast<size_t>(B) * H_v * nc * bb;
+  const size_t blocks = static_cast<size_t>(B) * H_v * nc * bb;
+  const SegPlan sp = carry_segments(B, T, H_v, dk, dv, chunk);
+  if (sp.P < 3) return blocks;
+  return align256(blocks) + seg_bytes(sp, static_cast<long>(B) * H_v, dk, dv);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int io_bf16, hipStream_t stream) {

@@ -140,6 +140,15 @@ size_t gdr_prefill_workspace_size(const gdr_dims* dims, gdr_dtype io, gdr_gate g
  * does not pay off there.  The workspace is then not touched, but the same
  * size is still required.
  *
+ * Long sequences over few units (at most 64 sixteen-column state slices,
+ * B * H_v * dv / 16, and segments of at least 8 chunks) carry the state by a
+ * parallel scan instead of one walk: the carry over a range of chunks is an
+ * affine map of the state, S_out = M S_in + N, so the sequence is cut into
+ * segments whose maps are formed side by side, composed in fp32, and each
+ * segment is then run from its start state.  The workspace then also holds
+ * fp32 segment states and maps, which the size query includes.  The result
+ * matches the single walk to rounding.
+ *
  *   dims        B, T, H_qk, H_v, dk, dv, chunk
  *   io          dtype of q, k, v and o
  *   gate        see gdr_gate; gate_in shape [B,T,H_v,dk] or [B,T,H_v]

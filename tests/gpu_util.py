@@ -67,9 +67,10 @@ def new_workspace(B, T, H_qk, H_v, dk, dv, chunk, io, gate):
 
 
 def run_prefill(case: synth.Case, chunk=None, state_in="S0", scale=1.0, l2norm=True,
-                T_slice=None, inplace=False, on_device=False):
+                T_slice=None, inplace=False, on_device=False, o_fill=None):
     """Run gdr_prefill_chunked on a seeded case; returns (o, state) on the host
-    as float64, or as device tensors with on_device=True."""
+    as float64, or as device tensors with on_device=True.  o_fill: a value the
+    output is filled with before the call (NaN shows any element left unwritten)."""
     t = case.tensors
     sl = slice(None) if T_slice is None else T_slice
     q = to_dev(t["q"][:, sl])
@@ -86,6 +87,8 @@ def run_prefill(case: synth.Case, chunk=None, state_in="S0", scale=1.0, l2norm=T
     s_out = s_in if (inplace and s_in is not None) else torch.empty(
         (B, case.H_v, case.dk, case.dv), dtype=torch.float32, device=DEV)
     o = torch.empty((B, T, case.H_v, case.dv), dtype=io_dtype(case.io), device=DEV)
+    if o_fill is not None:  # every output element must then be written by the call
+        o.fill_(o_fill)
     ws = new_workspace(B, T, case.H_qk, case.H_v, case.dk, case.dv, C, case.io, case.gate)
     gdr.gdr_prefill_chunked(q, k, v, g, bl, s_in, s_out, o, ws, H_qk=case.H_qk, H_v=case.H_v,
                             dk=case.dk, dv=case.dv, chunk=C, gate=case.gate,
@@ -95,3 +98,26 @@ def run_prefill(case: synth.Case, chunk=None, state_in="S0", scale=1.0, l2norm=T
     if on_device:
         return o, s_out
     return to_host(o), to_host(s_out)
+
+
+def carry_segments(B, T, H_v, dk, dv, chunk):
+    """The library's choice of carry segments for a chunked prefill (1: one
+    walk over the sequence), mirrored from its host routing so that tests know
+    which cases take the segmented carry."""
+    NC = -(-T // chunk)
+    units = B * H_v
+    w_n, w_m = units * (dv // 16), units * (dk // 16)
+    if w_n > 64:
+        return 1
+    best = 1
+    for P in range(3, 17):
+        L = -(-NC // P)
+        if L < 8:
+            break
+        Pe = -(-NC // L)
+        if Pe < 3:
+            continue
+        if w_n + (Pe - 2) * (w_n + w_m) > 512:
+            break
+        best = Pe
+    return best

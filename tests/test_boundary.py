@@ -123,6 +123,29 @@ def test_workspace_size_query():
     assert size(T=64, chunk=64) == lib.gdr_prefill_workspace_size(ctypes.byref(_dims(T=64, chunk=64)), 1, 2)
 
 
+def test_workspace_size_segmented_carry():
+    """Long prefills over few units take the segmented carry: the size query
+    adds its fp32 segment states and maps (S and N: P x units x dk x dv, M:
+    P x units x dk x dk) after the chunk blocks, aligned to 256 bytes."""
+    from tests.gpu_util import carry_segments
+    lib = gdr.load_library()
+
+    def size(**kw):
+        return lib.gdr_prefill_workspace_size(ctypes.byref(_dims(**kw)), 1, 0)
+
+    kw = dict(B=1, H_qk=1, H_v=2, dk=128, dv=128, chunk=64)
+    block = size(T=64, **kw) // 2                  # one chunk block per unit
+    for T in (3000, 20000):
+        P = carry_segments(1, T, 2, 128, 128, 64)
+        assert P >= 3
+        blocks = 2 * (-(-T // 64)) * block
+        extra = P * 2 * 128 * (2 * 128 + 128) * 4
+        assert size(T=T, **kw) == -(-blocks // 256) * 256 + extra
+    # many units: one walk, chunk blocks only
+    assert carry_segments(1, 3000, 32, 128, 128, 64) == 1
+    assert size(T=3000, B=1, H_qk=16, H_v=32, dk=128, dv=128, chunk=64) == 32 * 47 * block
+
+
 def test_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError):
         gdr.load_library(tmp_path / "libgdr.so")

@@ -8,8 +8,8 @@ import torch
 import gated_delta_rule_40_amd as gdr
 import oracle
 from gated_delta_rule_40_amd import synth
-from tests.gpu_util import (DEV, TOL, announce, oracle_threads, rel, require_gpu, run_prefill,
-                            to_dev, to_host)
+from tests.gpu_util import (DEV, TOL, announce, carry_segments, oracle_threads, rel, require_gpu,
+                            run_prefill, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -266,6 +266,53 @@ def test_prefill_long_few_heads(T, chunk, gate, mode):
     eo, es = rel(o, o_ref), rel(S, S_ref)
     print(f"err o={eo:.3e} S={es:.3e}")
     assert eo < TOL[io] and es < TOL[io]
+
+
+@pytest.mark.parametrize("B,H_qk,H_v,dk,dv,chunk,T,io,gate,mode", [
+    (1, 1, 2, 128, 128, 64, 3000, "bf16", synth.GATE_CHANNEL, "s0"),
+    (1, 1, 4, 64, 32, 32, 2500, "f32", synth.GATE_SCALAR, "null"),
+    (1, 2, 4, 64, 64, 16, 1000, "bf16", synth.GATE_SCALAR_FUSED, "inplace"),
+    (2, 1, 2, 32, 64, 64, 4100, "bf16", synth.GATE_CHANNEL, "s0"),
+    (1, 1, 1, 16, 16, 64, 1700, "f32", synth.GATE_CHANNEL, "s0"),
+])
+def test_prefill_segmented_carry(B, H_qk, H_v, dk, dv, chunk, T, io, gate, mode):
+    """Few (b, h) units and a long sequence: the carry runs as a parallel scan
+    of its affine maps over sequence segments (segment 0 beside the maps of
+    the middle segments, the start states composed in fp32, then every later
+    segment again from its start state).  Checked against the oracle with a
+    nonzero, null or in-place initial state and a ragged last chunk."""
+    require_gpu()
+    P = carry_segments(B, T, H_v, dk, dv, chunk)
+    assert P >= 3, "case no longer takes the segmented carry"
+    case = synth.prefill_case("seg", 500 + T % 97, B, T, H_qk, H_v, dk, dv, chunk, io, gate,
+                              0.01, 0.3, 0.0 if mode == "null" else 0.3)
+    announce(f"prefill segmented carry P={P} io={io} B={B} T={T} H {H_qk}->{H_v} dk={dk} "
+             f"dv={dv} chunk={chunk} gate={gate} {mode}")
+    kw = {"inplace": True} if mode == "inplace" else ({"state_in": None} if mode == "null" else {})
+    o, S = run_prefill(case, o_fill=float("nan"), **kw)
+    o_ref, S_ref = _oracle(case)
+    eo, es = rel(o, o_ref), rel(S, S_ref)
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[io] and es < TOL[io]
+
+
+@pytest.mark.timeout(600)
+def test_prefill_segmented_carry_long():
+    """B=1, 4 value heads, dk=dv=128, T=20000 (313 chunks) in bf16 with a
+    channel gate: the longest segmented case, every output and the state
+    against the oracle."""
+    require_gpu()
+    B, T, H_qk, H_v = 1, 20000, 1, 4
+    P = carry_segments(B, T, H_v, 128, 128, 64)
+    assert P >= 3
+    case = synth.prefill_case("seglong", 520, B, T, H_qk, H_v, 128, 128, 64, "bf16",
+                              synth.GATE_CHANNEL, 0.001, 0.2, 0.02)
+    announce(f"prefill segmented carry long P={P} B=1 T=20000 H 1->4 dk=dv=128 bf16")
+    o, S = run_prefill(case, o_fill=float("nan"))
+    o_ref, S_ref = _oracle(case)
+    eo, es = rel(o, o_ref), rel(S, S_ref)
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
 def test_prefill_split_sequence_equals_whole():

@@ -1339,10 +1339,16 @@ hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
 // instead of P.  The maps use the same bf16 (or fp32) operands as the plain
 // carry, so the result matches it to rounding.
 // ---------------------------------------------------------------------------
-constexpr long kSegMaxPlainWgs = 64;  // plain carry workgroups (16-column slices) at most
-constexpr int kSegMinChunks = 8;      // chunks per segment at least
+// Limits measured at B=1, dk=dv=128 (eager prefills): a side-by-side launch of
+// up to 512 workgroups pays at any length; up to 1024 pays from 256 chunks
+// (H_v=8, T=32767: 495 -> 452 us; H_v=16: 938 -> 830 us) but not at 125
+// (H_v=8, T=8000: 103 -> 115 us).
+constexpr long kSegMaxPlainWgs = 128;   // plain carry workgroups (16-column slices) at most
+constexpr int kSegMinChunks = 8;        // chunks per segment at least
 constexpr int kSegMaxSegments = 16;
-constexpr long kSegMaxWgs = 512;      // workgroups of the side-by-side launch at most
+constexpr long kSegMaxWgs = 512;        // workgroups of the side-by-side launch at most ...
+constexpr long kSegMaxWgsLong = 1024;   // ... from kSegLongChunks chunks on
+constexpr int kSegLongChunks = 256;
 
 struct SegPlan {
   int P;        // segments (1: the plain carry)
@@ -1356,13 +1362,14 @@ SegPlan carry_segments(int B, int T, int H_v, int dk, int dv, int chunk) {
   const long w_n = units * (dv / 16);  // workgroups per segment of a dv-column job
   const long w_m = units * (dk / 16);  // of a dk-column (linear part) job
   if (dv < 16 || dk < 16 || w_n > kSegMaxPlainWgs) return plain;
+  const long max_wgs = NC >= kSegLongChunks ? kSegMaxWgsLong : kSegMaxWgs;
   SegPlan best = plain;
   for (int P = 3; P <= kSegMaxSegments; ++P) {
     const int L = (NC + P - 1) / P;
     if (L < kSegMinChunks) break;
     const int Pe = (NC + L - 1) / L;  // segments actually formed
     if (Pe < 3) continue;
-    if (w_n + (Pe - 2) * (w_n + w_m) > kSegMaxWgs) break;
+    if (w_n + (Pe - 2) * (w_n + w_m) > max_wgs) break;
     best = SegPlan{Pe, L};
   }
   return best;

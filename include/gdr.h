@@ -140,7 +140,7 @@ size_t gdr_prefill_workspace_size(const gdr_dims* dims, gdr_dtype io, gdr_gate g
  * does not pay off there.  The workspace is then not touched, but the same
  * size is still required.
  *
- * Long sequences over few units (at most 64 sixteen-column state slices,
+ * Long sequences over few units (at most 128 sixteen-column state slices,
  * B * H_v * dv / 16, and segments of at least 8 chunks) carry the state by a
  * parallel scan instead of one walk: the carry over a range of chunks is an
  * affine map of the state, S_out = M S_in + N, so the sequence is cut into

@@ -107,8 +107,9 @@ def carry_segments(B, T, H_v, dk, dv, chunk):
     NC = -(-T // chunk)
     units = B * H_v
     w_n, w_m = units * (dv // 16), units * (dk // 16)
-    if w_n > 64:
+    if w_n > 128:
         return 1
+    max_wgs = 1024 if NC >= 256 else 512
     best = 1
     for P in range(3, 17):
         L = -(-NC // P)
@@ -117,7 +118,7 @@ def carry_segments(B, T, H_v, dk, dv, chunk):
         Pe = -(-NC // L)
         if Pe < 3:
             continue
-        if w_n + (Pe - 2) * (w_n + w_m) > 512:
+        if w_n + (Pe - 2) * (w_n + w_m) > max_wgs:
             break
         best = Pe
     return best

@@ -50,10 +50,11 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t r, unsigned vo
                                          kNt ? 2 : 0);
 }
 
-template <int DK, int DVS>
+// NTM: threads per workgroup at most (256, or 64 for one wave per tile).
+template <int DK, int DVS, int NTM = 256>
 struct DecodeShape {
   static constexpr int C4 = DVS / 4;                          // float4 columns
-  static constexpr int RG = (DK < 256 / C4) ? DK : 256 / C4;  // row groups
+  static constexpr int RG = (DK < NTM / C4) ? DK : NTM / C4;  // row groups
   static constexpr int NT = C4 * RG;                          // threads
   static constexpr int RPT = DK / RG;                         // rows per thread
   static constexpr int NW = NT / 64;                          // waves
@@ -68,11 +69,11 @@ struct DecodeShape {
 // only evicts what the rest of the step needs, and streaming stores are
 // faster (B=160, 192, 256 at dk=dv=128: 12%, 19%, 18%; B=64 and 128: plain
 // 6% and 2% faster).
-template <typename IoT, int DK, int DVS, bool kChannel, bool kNtStore>
-__global__ __launch_bounds__((DecodeShape<DK, DVS>::NT))
+template <typename IoT, int DK, int DVS, bool kChannel, bool kNtStore, int NTM>
+__global__ __launch_bounds__((DecodeShape<DK, DVS, NTM>::NT))
 __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void decode_kernel(
     DecodeArgs a) {
-  using Sh = DecodeShape<DK, DVS>;
+  using Sh = DecodeShape<DK, DVS, NTM>;
   constexpr int C4 = Sh::C4, RPT = Sh::RPT, NW = Sh::NW;
   constexpr int NE = (DK + 63) / 64;  // head elements per lane of wave 0
   // Per-row vectors of the head, shared by the C4 lanes of each row group:
@@ -237,16 +238,19 @@ __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void
   p1 = lane_class_sum<C4>(p1);
   p2 = lane_class_sum<C4>(p2);
   p3 = lane_class_sum<C4>(p3);
-  if (lane < C4) red[0][wave][c4] = make_float4(p0, p1, p2, p3);
-  __syncthreads();
-  float4 vh4 = red[0][0][c4];
+  float4 vh4 = make_float4(p0, p1, p2, p3);  // one wave: every lane holds its columns' sums
+  if constexpr (NW > 1) {
+    if (lane < C4) red[0][wave][c4] = vh4;
+    __syncthreads();
+    vh4 = red[0][0][c4];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    float4 t = red[0][w][c4];
-    vh4.x += t.x;
-    vh4.y += t.y;
-    vh4.z += t.z;
-    vh4.w += t.w;
+    for (int w = 1; w < NW; ++w) {
+      float4 t = red[0][w][c4];
+      vh4.x += t.x;
+      vh4.y += t.y;
+      vh4.z += t.z;
+      vh4.w += t.w;
+    }
   }
   const float u0 = beta * (vv[0] - vh4.x), u1 = beta * (vv[1] - vh4.y);
   const float u2 = beta * (vv[2] - vh4.z), u3 = beta * (vv[3] - vh4.w);
@@ -271,17 +275,22 @@ __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void
   o1 = lane_class_sum<C4>(o1);
   o2 = lane_class_sum<C4>(o2);
   o3 = lane_class_sum<C4>(o3);
-  if (lane < C4) red[1][wave][c4] = make_float4(o0, o1, o2, o3);
-  __syncthreads();
+  float4 acc = make_float4(o0, o1, o2, o3);
+  if constexpr (NW > 1) {
+    if (lane < C4) red[1][wave][c4] = acc;
+    __syncthreads();
+  }
   if (tid < C4) {
-    float4 acc = red[1][0][c4];
+    if constexpr (NW > 1) {
+      acc = red[1][0][c4];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      float4 t = red[1][w][c4];
-      acc.x += t.x;
-      acc.y += t.y;
-      acc.z += t.z;
-      acc.w += t.w;
+      for (int w = 1; w < NW; ++w) {
+        float4 t = red[1][w][c4];
+        acc.x += t.x;
+        acc.y += t.y;
+        acc.z += t.z;
+        acc.w += t.w;
+      }
     }
     IoT* op = static_cast<IoT*>(a.o) + bh * a.dv + j0;
     store4<IoT>(op, a.scale * acc.x, a.scale * acc.y, a.scale * acc.z, a.scale * acc.w);
@@ -299,20 +308,31 @@ __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void
 constexpr unsigned kOccupancyPadBytes = 40 * 1024;
 constexpr unsigned kOccupancyPadMinGrid = 2048;
 
+// Grids of at most this many tiles (one per CU or fewer: the step is a
+// latency chain) run one wave per tile, so that both column sums stay within
+// the wave (no LDS exchange, no barrier).
+constexpr unsigned kOneWaveMaxGrid = 256;
+
+template <typename IoT, int DK, int DVS, bool kNtStore, int NTM>
+hipError_t launch_ntm(const DecodeArgs& a, unsigned grid, unsigned pad, hipStream_t stream) {
+  if (a.gate == GDR_GATE_CHANNEL)
+    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, true, kNtStore, NTM>), dim3(grid),
+                       dim3(DecodeShape<DK, DVS, NTM>::NT), pad, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, false, kNtStore, NTM>), dim3(grid),
+                       dim3(DecodeShape<DK, DVS, NTM>::NT), pad, stream, a);
+  return hipGetLastError();
+}
+
 template <typename IoT, int DK, int DVS, bool kNtStore>
 hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.H_v * (a.dv / DVS);
+  if (grid <= kOneWaveMaxGrid) return launch_ntm<IoT, DK, DVS, kNtStore, 64>(a, grid, 0, stream);
   const unsigned pad = (DK == 128 && DVS == 128 && !kNtStore && a.gate == GDR_GATE_CHANNEL &&
                         grid >= kOccupancyPadMinGrid)
                            ? kOccupancyPadBytes
                            : 0;
-  if (a.gate == GDR_GATE_CHANNEL)
-    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, true, kNtStore>), dim3(grid),
-                       dim3(DecodeShape<DK, DVS>::NT), pad, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<IoT, DK, DVS, false, kNtStore>), dim3(grid),
-                       dim3(DecodeShape<DK, DVS>::NT), pad, stream, a);
-  return hipGetLastError();
+  return launch_ntm<IoT, DK, DVS, kNtStore, 256>(a, grid, pad, stream);
 }
 
 template <typename IoT, int DK, int DVS>

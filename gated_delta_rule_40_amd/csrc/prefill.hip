@@ -20,7 +20,7 @@
 // diag(e^Gamma_L) S + (K e^(Gamma_L - Gamma))^T U with the decay factored out,
 // so the chunk needs no third exponential per element).
 //
-// Two kernels:
+// Kernels:
 //   chunk_prep   one workgroup per (b, h, chunk), all chunks in parallel:
 //                everything that does not depend on S -- Kt, Qt, Kh^T, Tb, P
 //                and e^Gamma_L -- written to the caller's workspace, one
@@ -32,6 +32,11 @@
 //                the workspace into registers: as soon as a phase has used
 //                its fragments, the same registers load that phase's
 //                fragments of the next chunk.
+//   carry_scan   for long sequences over few (b, h) units only: the carry is
+//                cut into sequence segments whose affine maps (M, N) are
+//                formed by the carry side by side, this kernel composes the
+//                segments' start states, and the segments then run in
+//                parallel (the segmented carry, below).
 // Dense products use MFMA (bf16 operands with fp32 accumulation for bf16 io,
 // fp32 MFMA for fp32 io); the triangular solve runs in fp32 in LDS.
 #include <type_traits>
@@ -653,8 +658,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, Chu
 // ---------------------------------------------------------------------------
 // chunk_carry
 //
-// One workgroup per (b, h, slice of DVS state columns); the slice of S lives in
-// MFMA accumulators for the whole sequence.  Every operand the workspace block
+// One workgroup per (b, h, slice of DVS state columns) and chunk range (the
+// whole sequence, or one segment of the segmented carry); the slice of S lives
+// in MFMA accumulators for the whole range.  Every operand the workspace block
 // holds is an A operand of some product, and each wave reads exactly the rows
 // of them its tiles need straight from global memory into registers (each
 // fragment one contiguous read, the block being in fragment order), ahead of

@@ -69,7 +69,7 @@ const char* gdr_strerror(int status) {
     case GDR_E_UNSUPPORTED: return "dk/dv must be 16, 32, 64 or 128 and chunk 16, 32 or 64";
     case GDR_E_WORKSPACE: return "workspace is NULL or smaller than gdr_prefill_workspace_size()";
     case GDR_E_HIP: return "HIP runtime error at kernel launch";
-    case GDR_E_ALIAS: return "output overlaps an input or the state";
+    case GDR_E_ALIAS: return "output or workspace overlaps an input or the state";
     case GDR_E_ALIGN: return "tensor pointer is not 16-byte aligned";
     default: return "unknown gdr status";
   }
@@ -160,6 +160,17 @@ int gdr_prefill_chunked(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const
         overlap(ro, range_of(state_out, state_bytes)) ||
         (state_in && overlap(ro, range_of(state_in, state_bytes))) ||
         overlap(ro, range_of(workspace, need)))
+      return GDR_E_ALIAS;
+    // The kernels write the workspace (chunk blocks, segment states and maps)
+    // while the inputs and the state are still being read.
+    const Range rw = range_of(workspace, need);
+    if (overlap(rw, range_of(q, B * T * d.H_qk * d.dk * es)) ||
+        overlap(rw, range_of(k, B * T * d.H_qk * d.dk * es)) ||
+        overlap(rw, range_of(v, B * T * Hv * d.dv * es)) ||
+        overlap(rw, range_of(gate_in, gate_elems * sizeof(float))) ||
+        overlap(rw, range_of(beta_logit, B * T * Hv * sizeof(float))) ||
+        overlap(rw, range_of(state_out, state_bytes)) ||
+        (state_in && overlap(rw, range_of(state_in, state_bytes))))
       return GDR_E_ALIAS;
   }
 

@@ -82,7 +82,7 @@ typedef enum gdr_status {
   GDR_E_UNSUPPORTED = -4, /* dk/dv/chunk outside the compiled set               */
   GDR_E_WORKSPACE = -5,   /* workspace NULL or smaller than the size query      */
   GDR_E_HIP = -6,         /* the HIP runtime reported an error at launch        */
-  GDR_E_ALIAS = -7,       /* o overlaps an input or the state                   */
+  GDR_E_ALIAS = -7,       /* o or the workspace overlaps an input or the state  */
   GDR_E_ALIGN = -8        /* a tensor is not 16-byte aligned                    */
 } gdr_status;
 
@@ -160,8 +160,9 @@ size_t gdr_prefill_workspace_size(const gdr_dims* dims, gdr_dtype io, gdr_gate g
  *   state_out   [B,H_v,dk,dv] fp32 final state; may equal state_in
  *   o           [B,T,H_v,dv] io dtype; must not overlap any input or the state
  *   workspace   device memory of at least gdr_prefill_workspace_size() bytes,
- *               16-byte aligned, contents need not be initialised; it may be
- *               reused once the enqueued work has finished
+ *               16-byte aligned, contents need not be initialised; it must not
+ *               overlap any input, o or the state, and may be reused once the
+ *               enqueued work has finished
  *   T == 0      copies state_in to state_out (zeros when state_in is NULL)
  */
 int gdr_prefill_chunked(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const void* q,

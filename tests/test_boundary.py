@@ -103,6 +103,10 @@ def test_decode_validation(case, expect):
     (dict(v=A + 0x2000004), "ALIGN"),
     (dict(o=A + 0x2000000), "ALIAS"),              # o on top of v
     (dict(o=A + 0x10000000), "ALIAS"),             # o on top of the workspace
+    (dict(ws=A + 0x1000000), "ALIAS"),             # workspace on top of k
+    (dict(ws=A + 0x3000000), "ALIAS"),             # workspace on top of the gate
+    (dict(ws=A + 0x5000000), "ALIAS"),             # workspace on top of state_in
+    (dict(ws=A + 0x6000000), "ALIAS"),             # workspace on top of state_out
     (dict(dims=_dims(B=0)), "OK"),
     (dict(dims=_dims(T=0), s_in=A + 0x6000000), "OK"),   # T=0, in place: nothing to copy
 ])

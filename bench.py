@@ -16,6 +16,10 @@ Two legs, both on seeded synthetic inputs already resident in HBM:
            dk=dv=128, bf16, channelwise gate, zero initial state.  Reported as
            tokens/s, with the fraction of the HBM and bf16 MFMA peaks.
 
+Opt-in legs: sweep (T decode steps against one prefill), segmented (B=1,
+H 2 -> 4, T=32767: the long prefill over few heads that takes the segmented
+carry, under "prefill_segmented") and copy (HBM-counter calibration).
+
 Prints one JSON line.  `value` is the decode GB/s; the prefill figures sit
 under "prefill".  Each leg carries its roofline (kernel time from HIP events
 recorded around every launch on the launch stream) and the fp64 CPU oracle
@@ -344,6 +348,41 @@ def bench_prefill(reps, warm):
     )
 
 
+def bench_prefill_segmented(reps=4, warm=1):
+    """A long prefill over few heads, where the carry runs as a parallel scan
+    of per-segment affine maps: B=1, H_qk=2 -> H_v=4, dk=dv=128, T=32767,
+    chunk 64, bf16, channelwise gate with log-decay -U(0.001, 0.2), nonzero
+    initial state.  Graph replay of `reps` calls, as in the prefill leg."""
+    B, T, H_qk, H_v, dk, dv, C = 1, 32767, 2, 4, 128, 128, 64
+    case = synth.prefill_case("bench_seg", 9, B, T, H_qk, H_v, dk, dv, C, "bf16",
+                              synth.GATE_CHANNEL, 0.001, 0.2, 0.02)
+    t = case.tensors
+    q, k, v = up(t["q"]), up(t["k"]), up(t["v"])
+    g, bl, S0 = up(t["gate_in"]), up(t["beta_logit"]), up(t["S0"])
+    S = torch.empty_like(S0)
+    o = torch.empty((B, T, H_v, dv), dtype=torch.bfloat16, device=DEV)
+    ws_bytes = gdr.gdr_prefill_workspace_size(B, T, H_qk, H_v, dk, dv, C, torch.bfloat16,
+                                              case.gate)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    kw = dict(H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, chunk=C, gate=case.gate)
+
+    def run_all():
+        for _ in range(reps):
+            gdr.gdr_prefill_chunked(q, k, v, g, bl, S0, S, o, ws, **kw)
+
+    for _ in range(warm):
+        run_all()
+    sec = graph_us(run_all, reps=2) / reps / 1e6
+    return dict(
+        value=B * T / sec, unit="tokens/s", ms_per_call=sec * 1e3,
+        timing=f"HIP events around graph replays of {reps} calls, / calls",
+        workload=f"prefill_few_heads: B={B}, T={T}, H_qk={H_qk}->H_v={H_v}, dk=dv={dk}, "
+                 f"chunk {C}, channelwise gate, bf16 io, nonzero initial state "
+                 f"(segmented carry)",
+        workspace_bytes=ws_bytes,
+    )
+
+
 # ---------------------------------------------------------------------------
 # T-sweep: T decode steps against one chunked prefill of the same T tokens
 # ---------------------------------------------------------------------------
@@ -491,7 +530,8 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--legs", default="decode,prefill",
                     help="comma list of decode, prefill, sweep (T-sweep of decode steps against "
-                         "one prefill), copy (HBM-counter calibration)")
+                         "one prefill), segmented (a long prefill over few heads: the "
+                         "segmented carry), copy (HBM-counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time box of each CPU-oracle baseline (0 disables)")
     args = ap.parse_args()
@@ -523,6 +563,12 @@ def main():
     if "sweep" in legs:
         sweep = bench_sweep()
         print("[bench] sweep done", file=sys.stderr, flush=True)
+
+    seg = None
+    if "segmented" in legs:
+        seg = bench_prefill_segmented()
+        print(f"[bench] segmented prefill done: {seg['value']:.3e} tok/s", file=sys.stderr,
+              flush=True)
 
     if "copy" in legs:
         n = copy_calibration()
@@ -566,6 +612,8 @@ def main():
                         "roofline": pre["roofline"], "cpu_baseline": cpu_pre})
     if sweep is not None:
         out["sweep"] = sweep
+    if seg is not None:
+        out["prefill_segmented"] = seg
     print(json.dumps(out), flush=True)
 
 

@@ -315,6 +315,35 @@ def test_prefill_segmented_carry_long():
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("H_v", [2, 40])
+def test_prefill_weak_decay_long(H_v):
+    """Weak decay (log-decay -U(0.0005, 0.005)) over T=20000 with a nonzero
+    initial state: the state carries across the whole sequence, so rounding
+    compounds over 313 chunks.  With 2 value heads the carry is segmented (16
+    segments, each map's rounding carried through the composed start states);
+    with 40 it is one walk.  Both against the oracle, on sampled heads for the
+    wider case."""
+    require_gpu()
+    B, T, dk, dv, C = 1, 20000, 64, 64, 64
+    H_qk = H_v // 2
+    P = carry_segments(B, T, H_v, dk, dv, C)
+    assert (P >= 3) == (H_v == 2)
+    case = synth.prefill_case("weak", 530 + H_v, B, T, H_qk, H_v, dk, dv, C, "bf16",
+                              synth.GATE_CHANNEL, 0.0005, 0.005, 0.05)
+    announce(f"prefill weak decay T=20000 H {H_qk}->{H_v} dk=dv=64 segments={P}")
+    o, S = run_prefill(case, o_fill=float("nan"))
+    if H_v == 2:
+        o_ref, S_ref = _oracle(case)
+        eo, es = rel(o, o_ref), rel(S, S_ref)
+    else:
+        ref = _oracle(case, heads=[(0, 0), (0, 17), (0, 39)])
+        eo = max(rel(o[b, :, h], o_r[0, :, 0]) for (b, h), (o_r, _) in ref.items())
+        es = max(rel(S[b, h], S_r[0, 0]) for (b, h), (_, S_r) in ref.items())
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
 def test_prefill_split_sequence_equals_whole():
     require_gpu()
     case = synth.prefill_case("split", 61, 2, 150, 2, 2, 64, 64, 32, "f32", synth.GATE_CHANNEL,

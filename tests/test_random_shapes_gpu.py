@@ -12,7 +12,8 @@ import torch
 import gated_delta_rule_40_amd as gdr
 import oracle
 from gated_delta_rule_40_amd import synth
-from tests.gpu_util import DEV, TOL, announce, io_dtype, rel, require_gpu, run_prefill, to_dev, to_host
+from tests.gpu_util import (DEV, TOL, announce, carry_segments, io_dtype, rel, require_gpu,
+                            run_prefill, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,3 +91,40 @@ def test_random_shape_prefill_and_decode(seed):
         assert rel(to_host(o_d), o_r) < tol, (i, rel(to_host(o_d), o_r))
     torch.cuda.synchronize()
     assert rel(to_host(S_d), S_o) < tol
+
+
+def draw_long(seed: int) -> dict:
+    """A long sequence over few (b, h) units: shapes that take the segmented
+    carry (the draw is repeated until it does)."""
+    r = np.random.default_rng(3000 + seed)
+    while True:
+        H_qk = int(r.integers(1, 3))
+        p = dict(B=int(r.integers(1, 3)), T=int(r.integers(900, 3200)), H_qk=H_qk,
+                 H_v=H_qk * int(r.integers(1, 3)), dk=int(r.choice(DIMS)),
+                 dv=int(r.choice(DIMS)), chunk=int(r.choice([16, 32, 64])),
+                 gate=int(r.choice(GATES)), io=str(r.choice(["f32", "bf16"])),
+                 s0=float(r.choice([0.0, 0.3])), inplace=bool(r.integers(0, 2)))
+        if carry_segments(p["B"], p["T"], p["H_v"], p["dk"], p["dv"], p["chunk"]) >= 3:
+            return p
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_long_few_heads(seed):
+    """Seeded long prefills over few heads (segmented carry), crossed over
+    head sizes, chunk, gate kind, io dtype and initial state (zero, nonzero,
+    in place), every output checked (NaN-filled beforehand) against the
+    oracle."""
+    require_gpu()
+    p = draw_long(seed)
+    P = carry_segments(p["B"], p["T"], p["H_v"], p["dk"], p["dv"], p["chunk"])
+    announce(f"random long few-head seed={seed} segments={P}: {p}")
+    case = synth.prefill_case(f"rlong{seed}", 4000 + seed, p["B"], p["T"], p["H_qk"], p["H_v"],
+                              p["dk"], p["dv"], p["chunk"], p["io"], p["gate"], 0.001, 0.2,
+                              p["s0"])
+    t = case.tensors
+    o_ref, S_ref = oracle.sequence(case.values("q"), case.values("k"), case.values("v"),
+                                   case.gate, t["gate_in"], t["beta_logit"], t["S0"],
+                                   A_log=t["A_log"], dt_bias=t["dt_bias"], threads=4)
+    o, S = run_prefill(case, inplace=p["inplace"], o_fill=float("nan"))
+    tol = TOL[p["io"]]
+    assert rel(o, o_ref) < tol and rel(S, S_ref) < tol, (rel(o, o_ref), rel(S, S_ref))

@@ -129,6 +129,25 @@ def test_decode_slice_widths_bf16(B, rows):
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,io,gate", [
+    (80, "f32", synth.GATE_SCALAR),        # 2560 tiles, fp32 rows, scalar gate
+    (64, "bf16", synth.GATE_SCALAR_FUSED),  # 2048 tiles, fused gate (full occupancy)
+    (72, "bf16", synth.GATE_CHANNEL),       # 2304 tiles, channel gate (at most 3 per CU)
+    (36, "f32", synth.GATE_CHANNEL),        # 1152 tiles, below the occupancy cap
+])
+def test_decode_large_grids(B, io, gate):
+    """Whole 128 x 128 tiles (H 16 -> 32, dk=dv=128) on large grids, for each
+    launch shape of the step: fp32 or bf16 rows, scalar, fused or channel
+    gate, with and without the occupancy cap; 2 steps, sampled batch rows."""
+    case = synth.decode_case(f"grid{B}", 60 + B, B, 2, 16, 32, 128, 128, io, gate, 0.01, 0.5,
+                             0.02)
+    announce(f"decode {io} B={B} gate={gate} H 16->32 dk=dv=128 steps=2")
+    eo, es = _decode_run(case, 2, rows=[0, B // 2, B - 1])
+    print(f"err o={eo:.3e} S={es:.3e}")
+    assert eo < TOL[io] and es < TOL[io]
+
+
 def test_decode_write_then_read_identity():
     """beta = 1 (large logit), q = k: the value just written is read back."""
     case = synth.decode_case("ident", 41, 3, 3, 2, 4, 64, 64, "f32", synth.GATE_CHANNEL,

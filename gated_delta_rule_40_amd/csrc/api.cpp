@@ -26,6 +26,12 @@ Range range_of(const void* p, size_t bytes) {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
+bool overlaps_any(Range a, const Range* others, int n) {
+  for (int i = 0; i < n; ++i)
+    if (overlap(a, others[i])) return true;
+  return false;
+}
+
 int check_sizes(const gdr_dims* d, gdr_dtype io, gdr_gate gate, bool prefill) {
   if (!d) return GDR_E_NULL;
   if (io != GDR_F32 && io != GDR_BF16) return GDR_E_DTYPE;
@@ -69,7 +75,7 @@ const char* gdr_strerror(int status) {
     case GDR_E_UNSUPPORTED: return "dk/dv must be 16, 32, 64 or 128 and chunk 16, 32 or 64";
     case GDR_E_WORKSPACE: return "workspace is NULL or smaller than gdr_prefill_workspace_size()";
     case GDR_E_HIP: return "HIP runtime error at kernel launch";
-    case GDR_E_ALIAS: return "output or workspace overlaps an input or the state";
+    case GDR_E_ALIAS: return "an output, the state or the workspace overlaps a buffer it must not";
     case GDR_E_ALIGN: return "tensor pointer is not 16-byte aligned";
     default: return "unknown gdr status";
   }
@@ -92,12 +98,17 @@ int gdr_decode_step(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const voi
   const size_t es = io == GDR_BF16 ? 2 : 4;
   const size_t B = d.B, Hv = d.H_v;
   const Range ro = range_of(o, B * Hv * d.dv * es);
+  const Range rs = range_of(state, B * Hv * d.dk * d.dv * sizeof(float));
   const size_t gate_elems = gate == GDR_GATE_CHANNEL ? B * Hv * d.dk : B * Hv;
-  if (overlap(ro, range_of(qkv, B * (2 * d.H_qk * d.dk + Hv * d.dv) * es)) ||
-      overlap(ro, range_of(state, B * Hv * d.dk * d.dv * sizeof(float))) ||
-      overlap(ro, range_of(gate_in, gate_elems * sizeof(float))) ||
-      overlap(ro, range_of(beta_logit, B * Hv * sizeof(float))))
-    return GDR_E_ALIAS;
+  // Inputs the kernel reads while o and the state are being written.
+  Range ins[5] = {range_of(qkv, B * (2 * d.H_qk * d.dk + Hv * d.dv) * es),
+                  range_of(gate_in, gate_elems * sizeof(float)),
+                  range_of(beta_logit, B * Hv * sizeof(float)), Range{0, 0}, Range{0, 0}};
+  if (gate == GDR_GATE_SCALAR_FUSED) {
+    ins[3] = range_of(A_log, Hv * sizeof(float));
+    ins[4] = range_of(dt_bias, Hv * sizeof(float));
+  }
+  if (overlap(ro, rs) || overlaps_any(ro, ins, 5) || overlaps_any(rs, ins, 5)) return GDR_E_ALIAS;
 
   gdr::DecodeArgs a;
   a.qkv = qkv;
@@ -150,29 +161,36 @@ int gdr_prefill_chunked(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const
     if (!workspace || workspace_bytes < need) return GDR_E_WORKSPACE;
     if (!aligned(workspace, 16)) return GDR_E_ALIGN;
     const size_t es = io == GDR_BF16 ? 2 : 4;
-    const Range ro = range_of(o, B * T * Hv * d.dv * es);
     const size_t gate_elems = gate == GDR_GATE_CHANNEL ? B * T * Hv * d.dk : B * T * Hv;
-    if (overlap(ro, range_of(q, B * T * d.H_qk * d.dk * es)) ||
-        overlap(ro, range_of(k, B * T * d.H_qk * d.dk * es)) ||
-        overlap(ro, range_of(v, B * T * Hv * d.dv * es)) ||
-        overlap(ro, range_of(gate_in, gate_elems * sizeof(float))) ||
-        overlap(ro, range_of(beta_logit, B * T * Hv * sizeof(float))) ||
-        overlap(ro, range_of(state_out, state_bytes)) ||
-        (state_in && overlap(ro, range_of(state_in, state_bytes))) ||
-        overlap(ro, range_of(workspace, need)))
-      return GDR_E_ALIAS;
-    // The kernels write the workspace (chunk blocks, segment states and maps)
-    // while the inputs and the state are still being read.
+    // Read-only inputs; o, the workspace and state_out are written while
+    // they (and state_in) are still being read.
+    Range ins[8] = {range_of(q, B * T * d.H_qk * d.dk * es),
+                    range_of(k, B * T * d.H_qk * d.dk * es),
+                    range_of(v, B * T * Hv * d.dv * es),
+                    range_of(gate_in, gate_elems * sizeof(float)),
+                    range_of(beta_logit, B * T * Hv * sizeof(float)),
+                    state_in ? range_of(state_in, state_bytes) : Range{0, 0},
+                    Range{0, 0}, Range{0, 0}};
+    if (gate == GDR_GATE_SCALAR_FUSED) {
+      ins[6] = range_of(A_log, Hv * sizeof(float));
+      ins[7] = range_of(dt_bias, Hv * sizeof(float));
+    }
+    const Range ro = range_of(o, B * T * Hv * d.dv * es);
     const Range rw = range_of(workspace, need);
-    if (overlap(rw, range_of(q, B * T * d.H_qk * d.dk * es)) ||
-        overlap(rw, range_of(k, B * T * d.H_qk * d.dk * es)) ||
-        overlap(rw, range_of(v, B * T * Hv * d.dv * es)) ||
-        overlap(rw, range_of(gate_in, gate_elems * sizeof(float))) ||
-        overlap(rw, range_of(beta_logit, B * T * Hv * sizeof(float))) ||
-        overlap(rw, range_of(state_out, state_bytes)) ||
-        (state_in && overlap(rw, range_of(state_in, state_bytes))))
+    const Range rso = range_of(state_out, state_bytes);
+    if (overlap(ro, rw) || overlap(ro, rso) || overlap(rw, rso) || overlaps_any(ro, ins, 8) ||
+        overlaps_any(rw, ins, 8))
       return GDR_E_ALIAS;
+    // state_out may be state_in itself (every state slice is read before it
+    // is rewritten), but no other input.
+    ins[5] = Range{0, 0};
+    if (overlaps_any(rso, ins, 8)) return GDR_E_ALIAS;
   }
+  // state_out either is state_in or lies apart from it: a shifted overlap
+  // would have one workgroup read a state row that another has rewritten.
+  if (state_in && state_in != state_out &&
+      overlap(range_of(state_in, state_bytes), range_of(state_out, state_bytes)))
+    return GDR_E_ALIAS;
 
   gdr::PrefillArgs a;
   a.q = q;

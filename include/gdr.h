@@ -82,7 +82,8 @@ typedef enum gdr_status {
   GDR_E_UNSUPPORTED = -4, /* dk/dv/chunk outside the compiled set               */
   GDR_E_WORKSPACE = -5,   /* workspace NULL or smaller than the size query      */
   GDR_E_HIP = -6,         /* the HIP runtime reported an error at launch        */
-  GDR_E_ALIAS = -7,       /* o or the workspace overlaps an input or the state  */
+  GDR_E_ALIAS = -7,       /* o, the state or the workspace overlaps a buffer    */
+                          /* it must not (see each entry point)                 */
   GDR_E_ALIGN = -8        /* a tensor is not 16-byte aligned                    */
 } gdr_status;
 
@@ -105,8 +106,10 @@ typedef enum gdr_status {
  *               each head's channels contiguous
  *   A_log, dt_bias  [H_v] fp32 for GDR_GATE_SCALAR_FUSED, else ignored
  *   beta_logit  [B,H_v] fp32
- *   state       [B,H_v,dk,dv] fp32, read and updated IN PLACE
- *   o           [B,H_v,dv] io dtype, written; must not overlap qkv or state
+ *   state       [B,H_v,dk,dv] fp32, read and updated IN PLACE; must not
+ *               overlap qkv, gate_in, A_log, dt_bias or beta_logit
+ *   o           [B,H_v,dv] io dtype, written; must not overlap the state or
+ *               any input
  *   scale       output multiplier
  *   l2norm_qk   nonzero: normalise q and k rows; zero: use them as given
  */
@@ -157,7 +160,9 @@ size_t gdr_prefill_workspace_size(const gdr_dims* dims, gdr_dtype io, gdr_gate g
  *   A_log, dt_bias  [H_v] fp32 for GDR_GATE_SCALAR_FUSED, else ignored
  *   beta_logit  [B,T,H_v] fp32
  *   state_in    [B,H_v,dk,dv] fp32 initial state, or NULL for zeros
- *   state_out   [B,H_v,dk,dv] fp32 final state; may equal state_in
+ *   state_out   [B,H_v,dk,dv] fp32 final state; either equal to state_in
+ *               (in place) or not overlapping it, and not overlapping any
+ *               other input
  *   o           [B,T,H_v,dv] io dtype; must not overlap any input or the state
  *   workspace   device memory of at least gdr_prefill_workspace_size() bytes,
  *               16-byte aligned, contents need not be initialised; it must not

@@ -8,8 +8,9 @@
  *
  * What it computes, and where each step is defined:
  *
- *   - "Q/K/V split, L2 normalization, head repeat, gating computation, and
- *     delta-rule recurrent state update" for one decode token
+ *   - The fused decode step for one token: split of the packed row into
+ *     q, k and v, normalisation of q and k, head repeat, the gates, and the
+ *     state update
  *       [page "Add fused GatedDeltaNet decode Triton kernel" (executorch
  *        PR #18865), PR summary].
  *   - The per-token state update: decay, predicted value from the decayed

@@ -67,6 +67,9 @@ def prefill(dims, io=0, gate=0, q=A, k=A + 0x1000000, v=A + 0x2000000, g=A + 0x3
                                    None)
 
 
+# Every case must fail validation or have nothing to launch (B = 0, or T = 0
+# in place): the addresses are fake, so a case that passed validation would
+# launch kernels on them.
 @pytest.mark.parametrize("case,expect", [
     (dict(dims=None), "NULL"),
     (dict(io=2), "DTYPE"),
@@ -83,6 +86,11 @@ def prefill(dims, io=0, gate=0, q=A, k=A + 0x1000000, v=A + 0x2000000, g=A + 0x3
     (dict(st=A + 0x300004), "ALIGN"),
     (dict(o=A + 0x300000), "ALIAS"),              # o on top of the state
     (dict(o=A), "ALIAS"),                         # o on top of qkv
+    (dict(st=A), "ALIAS"),                        # in-place state on top of qkv
+    (dict(st=A + 0x100000), "ALIAS"),             # ... on top of the gate
+    (dict(st=A + 0x200000 - 0x100), "ALIAS"),     # ... reaching into beta_logit
+    (dict(gate=2, Al=A + 0x300040, dt=A + 0x500000), "ALIAS"),   # A_log inside the state
+    (dict(gate=2, Al=A + 0x500000, dt=A + 0x4000000), "ALIAS"),  # dt_bias under o
     (dict(dims=_dims(B=0)), "OK"),                # nothing to do, nothing launched
 ])
 def test_decode_validation(case, expect):
@@ -107,8 +115,17 @@ def test_decode_validation(case, expect):
     (dict(ws=A + 0x3000000), "ALIAS"),             # workspace on top of the gate
     (dict(ws=A + 0x5000000), "ALIAS"),             # workspace on top of state_in
     (dict(ws=A + 0x6000000), "ALIAS"),             # workspace on top of state_out
+    (dict(s_out=A + 0x5000100), "ALIAS"),          # state_out shifted into state_in
+    (dict(s_out=A + 0x5000000 - 0x100), "ALIAS"),  # ... and the other way round
+    (dict(s_out=A + 0x2000000), "ALIAS"),          # state_out on top of v
+    (dict(s_out=A + 0x1000000), "ALIAS"),          # ... of k
+    (dict(s_out=A + 0x4000000), "ALIAS"),          # ... of beta_logit
+    (dict(gate=2, Al=A + 0x7000010, dt=A + 0x8000000), "ALIAS"),  # A_log under o
+    (dict(gate=2, Al=A + 0x8000000, dt=A + 0x10000000), "ALIAS"),  # dt_bias in the workspace
+    (dict(gate=2, Al=A + 0x6000000, dt=A + 0x8000000), "ALIAS"),  # A_log under state_out
     (dict(dims=_dims(B=0)), "OK"),
     (dict(dims=_dims(T=0), s_in=A + 0x6000000), "OK"),   # T=0, in place: nothing to copy
+    (dict(dims=_dims(T=0), s_out=A + 0x5000100), "ALIAS"),  # T=0, shifted copy
 ])
 def test_prefill_validation(case, expect):
     kw = dict(case)

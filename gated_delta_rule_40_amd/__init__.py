@@ -8,6 +8,8 @@ binding with the same entry-point names, and the seeded input generator.
     gdr_decode_step             one fused token (T = 1), state updated in place
     gdr_prefill_chunked         T tokens, chunkwise WY/UT form
     gdr_prefill_workspace_size  bytes of workspace the prefill needs
+    gdr_prefill_chunked_noalloc the prefill on the library's own device scratch
+                                (for callers that cannot allocate)
     gdr_strerror                text of a status code
 """
 from .binding import (  # noqa: F401
@@ -20,6 +22,7 @@ from .binding import (  # noqa: F401
     GdrError,
     gdr_decode_step,
     gdr_prefill_chunked,
+    gdr_prefill_chunked_noalloc,
     gdr_prefill_workspace_size,
     gdr_strerror,
     load_library,

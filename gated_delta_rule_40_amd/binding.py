@@ -21,7 +21,8 @@ GDR_OK = 0
 
 LIB_PATH = Path(__file__).resolve().parent / "libgdr.so"
 EXPORTED = ("gdr_decode_step", "gdr_prefill_workspace_size", "gdr_prefill_chunked",
-            "gdr_strerror")
+            "gdr_prefill_chunked_noalloc", "gdr_strerror")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # GDR_NOALLOC_SCRATCH_BYTES
 
 
 class GdrError(RuntimeError):
@@ -56,6 +57,9 @@ def load_library(path: Path | str | None = None):
     lib.gdr_prefill_chunked.argtypes = [dims_p, i32, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
                                         ctypes.c_float, i32, vp, ctypes.c_size_t, vp]
     lib.gdr_prefill_chunked.restype = i32
+    lib.gdr_prefill_chunked_noalloc.argtypes = [dims_p, i32, i32, vp, vp, vp, fp, fp, fp, fp, fp,
+                                                fp, vp, ctypes.c_float, i32, vp]
+    lib.gdr_prefill_chunked_noalloc.restype = i32
     lib.gdr_strerror.argtypes = [i32]
     lib.gdr_strerror.restype = ctypes.c_char_p
     if path is None:
@@ -134,29 +138,15 @@ def gdr_prefill_workspace_size(B, T, H_qk, H_v, dk, dv, chunk, io_dtype, gate) -
                                                          int(gate)))
 
 
-def gdr_prefill_chunked(q, k, v, gate_in, beta_logit, state_in, state_out, o, workspace, *,
-                        H_qk, H_v, dk, dv, chunk, gate, A_log=None, dt_bias=None, scale=1.0,
-                        l2norm_qk=True, stream=None):
-    """Chunked prefill.  q, k [B,T,H_qk,dk], v [B,T,H_v,dv] (float32 or bfloat16),
-    gate_in [B,T,H_v,dk] or [B,T,H_v], beta_logit [B,T,H_v], state_in (or None)
-    and state_out [B,H_v,dk,dv] fp32, o [B,T,H_v,dv], workspace a uint8 tensor
-    of at least gdr_prefill_workspace_size() bytes."""
-    lib = load_library()
+def _prefill_args(q, k, v, gate_in, beta_logit, state_in, state_out, o, H_qk, H_v, dk, dv,
+                  gate, A_log, dt_bias):
     B, T = q.shape[0], q.shape[1]
     dev = q.device
-    io = _io_code(q.dtype)
     f32 = torch.float32
     gate_n = B * T * H_v * dk if gate == GDR_GATE_CHANNEL else B * T * H_v
     fused = gate == GDR_GATE_SCALAR_FUSED
-    if workspace is not None:
-        if workspace.device != dev or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on the same device")
-        ws_ptr = ctypes.c_void_p(workspace.data_ptr())
-        ws_bytes = workspace.numel() * workspace.element_size()
-    else:
-        ws_ptr, ws_bytes = None, 0
     st = B * H_v * dk * dv
-    args = (
+    return (
         _check(q, "q", B * T * H_qk * dk, q.dtype, dev),
         _check(k, "k", B * T * H_qk * dk, q.dtype, dev),
         _check(v, "v", B * T * H_v * dv, q.dtype, dev),
@@ -168,9 +158,46 @@ def gdr_prefill_chunked(q, k, v, gate_in, beta_logit, state_in, state_out, o, wo
         _check(state_out, "state_out", st, f32, dev),
         _check(o, "o", B * T * H_v * dv, q.dtype, dev),
     )
-    dims = gdr_dims(B, T, H_qk, H_v, dk, dv, chunk)
-    rc = lib.gdr_prefill_chunked(ctypes.byref(dims), io, int(gate), *args, float(scale),
-                                 int(bool(l2norm_qk)), ws_ptr, ctypes.c_size_t(ws_bytes),
-                                 _stream(dev, stream))
+
+
+def gdr_prefill_chunked(q, k, v, gate_in, beta_logit, state_in, state_out, o, workspace, *,
+                        H_qk, H_v, dk, dv, chunk, gate, A_log=None, dt_bias=None, scale=1.0,
+                        l2norm_qk=True, stream=None):
+    """Chunked prefill.  q, k [B,T,H_qk,dk], v [B,T,H_v,dv] (float32 or bfloat16),
+    gate_in [B,T,H_v,dk] or [B,T,H_v], beta_logit [B,T,H_v], state_in (or None)
+    and state_out [B,H_v,dk,dv] fp32, o [B,T,H_v,dv], workspace a uint8 tensor
+    of at least gdr_prefill_workspace_size() bytes."""
+    lib = load_library()
+    dev = q.device
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the same device")
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr())
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    args = _prefill_args(q, k, v, gate_in, beta_logit, state_in, state_out, o, H_qk, H_v, dk, dv,
+                         gate, A_log, dt_bias)
+    dims = gdr_dims(q.shape[0], q.shape[1], H_qk, H_v, dk, dv, chunk)
+    rc = lib.gdr_prefill_chunked(ctypes.byref(dims), _io_code(q.dtype), int(gate), *args,
+                                 float(scale), int(bool(l2norm_qk)), ws_ptr,
+                                 ctypes.c_size_t(ws_bytes), _stream(dev, stream))
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_prefill_chunked")
+
+
+def gdr_prefill_chunked_noalloc(q, k, v, gate_in, beta_logit, state_in, state_out, o, *,
+                                H_qk, H_v, dk, dv, chunk, gate, A_log=None, dt_bias=None,
+                                scale=1.0, l2norm_qk=True, stream=None):
+    """gdr_prefill_chunked with the library's own device scratch as workspace
+    (nothing is allocated; at most NOALLOC_SCRATCH_BYTES of workspace; calls
+    that overlap on one device race on the scratch)."""
+    lib = load_library()
+    args = _prefill_args(q, k, v, gate_in, beta_logit, state_in, state_out, o, H_qk, H_v, dk, dv,
+                         gate, A_log, dt_bias)
+    dims = gdr_dims(q.shape[0], q.shape[1], H_qk, H_v, dk, dv, chunk)
+    rc = lib.gdr_prefill_chunked_noalloc(ctypes.byref(dims), _io_code(q.dtype), int(gate), *args,
+                                         float(scale), int(bool(l2norm_qk)),
+                                         _stream(q.device, stream))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_prefill_chunked_noalloc")

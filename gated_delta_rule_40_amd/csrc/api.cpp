@@ -8,6 +8,9 @@
 #include "gdr.h"
 #include "gdr_internal.h"
 
+static_assert(GDR_NOALLOC_SCRATCH_BYTES == gdr::kNoallocScratchBytes,
+              "the header's scratch limit is the size of the device array");
+
 namespace {
 
 bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -62,6 +65,107 @@ int check_gate_ptrs(gdr_gate gate, const float* gate_in, const float* A_log,
   return GDR_OK;
 }
 
+// The arguments of one prefill call (everything but the workspace and stream).
+struct PrefillCall {
+  const gdr_dims* dims;
+  gdr_dtype io;
+  gdr_gate gate;
+  const void *q, *k, *v;
+  const float *gate_in, *A_log, *dt_bias, *beta_logit, *state_in;
+  float* state_out;
+  void* o;
+  float scale;
+  int l2norm_qk;
+};
+
+// Validates a prefill call.  own_scratch: the workspace is the library's own
+// scratch array (workspace and workspace_bytes are then ignored).  *need
+// receives the workspace bytes the call uses (0 when nothing is launched).
+int check_prefill(const PrefillCall& c, bool own_scratch, const void* workspace,
+                  size_t workspace_bytes, size_t* need) {
+  *need = 0;
+  int rc = check_sizes(c.dims, c.io, c.gate, true);
+  if (rc != GDR_OK) return rc;
+  const gdr_dims& d = *c.dims;
+  if (d.B == 0) return GDR_OK;
+  if (!c.state_out) return GDR_E_NULL;
+  if (!aligned(c.state_out, 16) || (c.state_in && !aligned(c.state_in, 16))) return GDR_E_ALIGN;
+  const size_t B = d.B, T = d.T, Hv = d.H_v;
+  const size_t state_bytes = B * Hv * d.dk * d.dv * sizeof(float);
+  if (T > 0) {
+    if (!c.q || !c.k || !c.v || !c.beta_logit || !c.o) return GDR_E_NULL;
+    rc = check_gate_ptrs(c.gate, c.gate_in, c.A_log, c.dt_bias);
+    if (rc != GDR_OK) return rc;
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.o, 16) ||
+        !aligned(c.beta_logit, 4))
+      return GDR_E_ALIGN;
+    *need = gdr::prefill_workspace_bytes(d.B, d.T, d.H_v, d.dk, d.dv, d.chunk, c.io == GDR_BF16);
+    if (!own_scratch) {
+      if (!workspace || workspace_bytes < *need) return GDR_E_WORKSPACE;
+      if (!aligned(workspace, 16)) return GDR_E_ALIGN;
+    }
+    const size_t es = c.io == GDR_BF16 ? 2 : 4;
+    const size_t gate_elems = c.gate == GDR_GATE_CHANNEL ? B * T * Hv * d.dk : B * T * Hv;
+    // Read-only inputs; o, the workspace and state_out are written while
+    // they (and state_in) are still being read.
+    Range ins[8] = {range_of(c.q, B * T * d.H_qk * d.dk * es),
+                    range_of(c.k, B * T * d.H_qk * d.dk * es),
+                    range_of(c.v, B * T * Hv * d.dv * es),
+                    range_of(c.gate_in, gate_elems * sizeof(float)),
+                    range_of(c.beta_logit, B * T * Hv * sizeof(float)),
+                    c.state_in ? range_of(c.state_in, state_bytes) : Range{0, 0},
+                    Range{0, 0}, Range{0, 0}};
+    if (c.gate == GDR_GATE_SCALAR_FUSED) {
+      ins[6] = range_of(c.A_log, Hv * sizeof(float));
+      ins[7] = range_of(c.dt_bias, Hv * sizeof(float));
+    }
+    const Range ro = range_of(c.o, B * T * Hv * d.dv * es);
+    const Range rw = own_scratch ? Range{0, 0} : range_of(workspace, *need);
+    const Range rso = range_of(c.state_out, state_bytes);
+    if (overlap(ro, rw) || overlap(ro, rso) || overlap(rw, rso) || overlaps_any(ro, ins, 8) ||
+        overlaps_any(rw, ins, 8))
+      return GDR_E_ALIAS;
+    // state_out may be state_in itself (every state slice is read before it
+    // is rewritten), but no other input.
+    ins[5] = Range{0, 0};
+    if (overlaps_any(rso, ins, 8)) return GDR_E_ALIAS;
+  }
+  // state_out either is state_in or lies apart from it: a shifted overlap
+  // would have one workgroup read a state row that another has rewritten.
+  if (c.state_in && c.state_in != c.state_out &&
+      overlap(range_of(c.state_in, state_bytes), range_of(c.state_out, state_bytes)))
+    return GDR_E_ALIAS;
+  return GDR_OK;
+}
+
+int launch(const PrefillCall& c, void* workspace, hipStream_t stream) {
+  const gdr_dims& d = *c.dims;
+  if (d.B == 0) return GDR_OK;
+  gdr::PrefillArgs a;
+  a.q = c.q;
+  a.k = c.k;
+  a.v = c.v;
+  a.gate_in = c.gate_in;
+  a.A_log = c.A_log;
+  a.dt_bias = c.dt_bias;
+  a.beta_logit = c.beta_logit;
+  a.state_in = c.state_in;
+  a.state_out = c.state_out;
+  a.o = c.o;
+  a.ws = workspace;
+  a.B = d.B;
+  a.T = d.T;
+  a.H_qk = d.H_qk;
+  a.H_v = d.H_v;
+  a.dk = d.dk;
+  a.dv = d.dv;
+  a.chunk = d.chunk;
+  a.gate = c.gate;
+  a.l2norm = c.l2norm_qk != 0;
+  a.scale = c.scale;
+  return gdr::launch_prefill(a, c.io == GDR_BF16, stream) == hipSuccess ? GDR_OK : GDR_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,6 +181,8 @@ const char* gdr_strerror(int status) {
     case GDR_E_HIP: return "HIP runtime error at kernel launch";
     case GDR_E_ALIAS: return "an output, the state or the workspace overlaps a buffer it must not";
     case GDR_E_ALIGN: return "tensor pointer is not 16-byte aligned";
+    case GDR_E_SCRATCH:
+      return "the call needs more workspace than the allocation-free entry point holds";
     default: return "unknown gdr status";
   }
 }
@@ -141,80 +247,29 @@ int gdr_prefill_chunked(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const
                         const float* dt_bias, const float* beta_logit, const float* state_in,
                         float* state_out, void* o, float scale, int l2norm_qk, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
-  int rc = check_sizes(dims, io, gate, true);
+  const PrefillCall c{dims, io, gate, q, k, v, gate_in, A_log, dt_bias, beta_logit, state_in,
+                      state_out, o, scale, l2norm_qk};
+  size_t need = 0;
+  int rc = check_prefill(c, false, workspace, workspace_bytes, &need);
   if (rc != GDR_OK) return rc;
-  const gdr_dims& d = *dims;
-  if (d.B == 0) return GDR_OK;
-  if (!state_out) return GDR_E_NULL;
-  if (!aligned(state_out, 16) || (state_in && !aligned(state_in, 16))) return GDR_E_ALIGN;
-  const size_t B = d.B, T = d.T, Hv = d.H_v;
-  const size_t state_bytes = B * Hv * d.dk * d.dv * sizeof(float);
-  if (T > 0) {
-    if (!q || !k || !v || !beta_logit || !o) return GDR_E_NULL;
-    rc = check_gate_ptrs(gate, gate_in, A_log, dt_bias);
-    if (rc != GDR_OK) return rc;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(beta_logit, 4))
-      return GDR_E_ALIGN;
-    const size_t need = gdr::prefill_workspace_bytes(d.B, d.T, d.H_v, d.dk, d.dv, d.chunk,
-                                                     io == GDR_BF16);
-    if (!workspace || workspace_bytes < need) return GDR_E_WORKSPACE;
-    if (!aligned(workspace, 16)) return GDR_E_ALIGN;
-    const size_t es = io == GDR_BF16 ? 2 : 4;
-    const size_t gate_elems = gate == GDR_GATE_CHANNEL ? B * T * Hv * d.dk : B * T * Hv;
-    // Read-only inputs; o, the workspace and state_out are written while
-    // they (and state_in) are still being read.
-    Range ins[8] = {range_of(q, B * T * d.H_qk * d.dk * es),
-                    range_of(k, B * T * d.H_qk * d.dk * es),
-                    range_of(v, B * T * Hv * d.dv * es),
-                    range_of(gate_in, gate_elems * sizeof(float)),
-                    range_of(beta_logit, B * T * Hv * sizeof(float)),
-                    state_in ? range_of(state_in, state_bytes) : Range{0, 0},
-                    Range{0, 0}, Range{0, 0}};
-    if (gate == GDR_GATE_SCALAR_FUSED) {
-      ins[6] = range_of(A_log, Hv * sizeof(float));
-      ins[7] = range_of(dt_bias, Hv * sizeof(float));
-    }
-    const Range ro = range_of(o, B * T * Hv * d.dv * es);
-    const Range rw = range_of(workspace, need);
-    const Range rso = range_of(state_out, state_bytes);
-    if (overlap(ro, rw) || overlap(ro, rso) || overlap(rw, rso) || overlaps_any(ro, ins, 8) ||
-        overlaps_any(rw, ins, 8))
-      return GDR_E_ALIAS;
-    // state_out may be state_in itself (every state slice is read before it
-    // is rewritten), but no other input.
-    ins[5] = Range{0, 0};
-    if (overlaps_any(rso, ins, 8)) return GDR_E_ALIAS;
-  }
-  // state_out either is state_in or lies apart from it: a shifted overlap
-  // would have one workgroup read a state row that another has rewritten.
-  if (state_in && state_in != state_out &&
-      overlap(range_of(state_in, state_bytes), range_of(state_out, state_bytes)))
-    return GDR_E_ALIAS;
+  return launch(c, workspace, stream);
+}
 
-  gdr::PrefillArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.gate_in = gate_in;
-  a.A_log = A_log;
-  a.dt_bias = dt_bias;
-  a.beta_logit = beta_logit;
-  a.state_in = state_in;
-  a.state_out = state_out;
-  a.o = o;
-  a.ws = workspace;
-  a.B = d.B;
-  a.T = d.T;
-  a.H_qk = d.H_qk;
-  a.H_v = d.H_v;
-  a.dk = d.dk;
-  a.dv = d.dv;
-  a.chunk = d.chunk;
-  a.gate = gate;
-  a.l2norm = l2norm_qk != 0;
-  a.scale = scale;
-  return gdr::launch_prefill(a, io == GDR_BF16, stream) == hipSuccess ? GDR_OK : GDR_E_HIP;
+int gdr_prefill_chunked_noalloc(const gdr_dims* dims, gdr_dtype io, gdr_gate gate,
+                                const void* q, const void* k, const void* v,
+                                const float* gate_in, const float* A_log, const float* dt_bias,
+                                const float* beta_logit, const float* state_in, float* state_out,
+                                void* o, float scale, int l2norm_qk, hipStream_t stream) {
+  const PrefillCall c{dims, io, gate, q, k, v, gate_in, A_log, dt_bias, beta_logit, state_in,
+                      state_out, o, scale, l2norm_qk};
+  size_t need = 0;
+  int rc = check_prefill(c, true, nullptr, 0, &need);
+  if (rc != GDR_OK) return rc;
+  if (need > gdr::kNoallocScratchBytes) return GDR_E_SCRATCH;
+  if (dims->B == 0) return GDR_OK;
+  void* ws = nullptr;
+  if (need > 0 && gdr::noalloc_scratch(&ws) != hipSuccess) return GDR_E_HIP;
+  return launch(c, ws, stream);
 }
 
 }  // extern "C"

@@ -51,6 +51,13 @@ struct PrefillArgs {
 size_t prefill_workspace_bytes(int B, int T, int H_v, int dk, int dv, int chunk, int io_bf16);
 hipError_t launch_prefill(const PrefillArgs& a, int io_bf16, hipStream_t stream);
 
+// The allocation-free prefill takes its workspace from a device array of this
+// many bytes (one per device, held until the process ends).
+constexpr size_t kNoallocScratchBytes = static_cast<size_t>(128) << 20;
+// Device address of the current device's array (resolved on the first call
+// on that device).
+hipError_t noalloc_scratch(void** ptr);
+
 // Short sequences token by token (the state tile held in registers over all
 // T tokens; the workspace is not used).  The prefill takes this path for
 // T <= recurrent_max_t(B, H_v) when the per-token vectors fit

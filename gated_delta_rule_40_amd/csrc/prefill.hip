@@ -39,6 +39,7 @@
 //                parallel (the segmented carry, below).
 // Dense products use MFMA (bf16 operands with fp32 accumulation for bf16 io,
 // fp32 MFMA for fp32 io); the triangular solve runs in fp32 in LDS.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -1480,6 +1481,33 @@ size_t prefill_workspace_bytes(int B, int T, int H_v, int dk, int dv, int chunk,
   const SegPlan sp = carry_segments(B, T, H_v, dk, dv, chunk);
   if (sp.P < 3) return blocks;
   return align256(blocks) + seg_bytes(sp, static_cast<long>(B) * H_v, dk, dv);
+}
+
+// Scratch of the allocation-free prefill entry point: the workspace of one
+// call at a time on each device (every call on a device shares it, so calls
+// that overlap on one device race).  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is resolved once per device
+// with hipGetSymbolAddress and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int io_bf16, hipStream_t stream) {

@@ -84,7 +84,9 @@ typedef enum gdr_status {
   GDR_E_HIP = -6,         /* the HIP runtime reported an error at launch        */
   GDR_E_ALIAS = -7,       /* o, the state or the workspace overlaps a buffer    */
                           /* it must not (see each entry point)                 */
-  GDR_E_ALIGN = -8        /* a tensor is not 16-byte aligned                    */
+  GDR_E_ALIGN = -8,       /* a tensor is not 16-byte aligned                    */
+  GDR_E_SCRATCH = -9      /* the call needs more workspace than the             */
+                          /* allocation-free entry point holds                  */
 } gdr_status;
 
 /*
@@ -175,6 +177,34 @@ int gdr_prefill_chunked(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const
                         const float* dt_bias, const float* beta_logit, const float* state_in,
                         float* state_out, void* o, float scale, int l2norm_qk, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdr_prefill_chunked_noalloc -- gdr_prefill_chunked without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results, validation and status codes as
+ * gdr_prefill_chunked, minus workspace / workspace_bytes.  The workspace is a
+ * device array inside the library, GDR_NOALLOC_SCRATCH_BYTES bytes on each
+ * device it runs on, held until the process ends; the library allocates and
+ * frees nothing on any call.  The first call on a device (the current device)
+ * looks up that device's array address.
+ *
+ *   - A call whose gdr_prefill_workspace_size() exceeds
+ *     GDR_NOALLOC_SCRATCH_BYTES returns GDR_E_SCRATCH and enqueues nothing
+ *     (B = 1, H_v = 32, dk = dv = 128, chunk 64, bf16 fits up to T = 4032).
+ *   - Every call on a device shares that device's array and leaves its
+ *     contents behind; no content needs to be cleared between calls.  Calls
+ *     that may run at the same time on one device (other streams, other
+ *     threads) RACE on the array: order them on one stream, or use
+ *     gdr_prefill_chunked with a workspace per concurrent call.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdr_prefill_chunked_noalloc(const gdr_dims* dims, gdr_dtype io, gdr_gate gate,
+                                const void* q, const void* k, const void* v,
+                                const float* gate_in, const float* A_log, const float* dt_bias,
+                                const float* beta_logit, const float* state_in, float* state_out,
+                                void* o, float scale, int l2norm_qk, hipStream_t stream);
 
 /* Static, human-readable text for a gdr_status value. */
 const char* gdr_strerror(int status);

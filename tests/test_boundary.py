@@ -14,7 +14,7 @@ from gated_delta_rule_40_amd.binding import gdr_dims
 
 HEADER = Path(__file__).resolve().parents[1] / "include" / "gdr.h"
 E = dict(OK=0, NULL=-1, SHAPE=-2, DTYPE=-3, UNSUPPORTED=-4, WORKSPACE=-5, HIP=-6, ALIAS=-7,
-         ALIGN=-8)
+         ALIGN=-8, SCRATCH=-9)
 A = 0x10000  # fake, 16-byte aligned device addresses: never dereferenced here
 
 
@@ -131,6 +131,58 @@ def test_prefill_validation(case, expect):
     kw = dict(case)
     dims = kw.pop("dims", _dims())
     assert prefill(dims, **kw) == E[expect]
+
+
+def prefill_noalloc(dims, io=0, gate=0, q=A, k=A + 0x1000000, v=A + 0x2000000, g=A + 0x3000000,
+                    Al=None, dt=None, bl=A + 0x4000000, s_in=A + 0x5000000, s_out=A + 0x6000000,
+                    o=A + 0x7000000):
+    lib = gdr.load_library()
+    return lib.gdr_prefill_chunked_noalloc(ctypes.byref(dims) if dims is not None else None, io,
+                                           gate, q, k, v, g, Al, dt, bl, s_in, s_out, o, 1.0, 1,
+                                           None)
+
+
+def _big(T):
+    return gdr_dims(1, T, 16, 32, 128, 128, 64)
+
+
+G = 1 << 30
+# fake addresses 1 GiB apart, so that tensors of the large cases do not overlap
+SPREAD = dict(q=A, k=A + G, v=A + 2 * G, g=A + 3 * G, bl=A + 4 * G, s_in=A + 5 * G,
+              s_out=A + 6 * G, o=A + 7 * G)
+
+
+# As above: only cases that fail validation or have nothing to launch.
+@pytest.mark.parametrize("case,expect", [
+    (dict(dims=None), "NULL"),
+    (dict(io=2), "DTYPE"),
+    (dict(dims=_dims(chunk=8)), "UNSUPPORTED"),
+    (dict(q=None), "NULL"),
+    (dict(s_out=None), "NULL"),
+    (dict(o=A + 0x2000000), "ALIAS"),
+    (dict(s_out=A + 0x5000100), "ALIAS"),
+    (dict(v=A + 0x2000004), "ALIGN"),
+    (dict(dims=_big(4033), io=1, **SPREAD), "SCRATCH"),   # 64 chunks x 32 heads x 66,048 B
+    (dict(dims=_big(32767), io=1, **SPREAD), "SCRATCH"),
+    (dict(dims=_big(4032), io=0, **SPREAD), "SCRATCH"),   # fp32 operands: twice the bytes
+    (dict(dims=_dims(B=0)), "OK"),
+    (dict(dims=_dims(T=0), s_in=A + 0x6000000), "OK"),
+])
+def test_prefill_noalloc_validation(case, expect):
+    kw = dict(case)
+    dims = kw.pop("dims", _dims())
+    assert prefill_noalloc(dims, **kw) == E[expect]
+
+
+def test_noalloc_limit_is_the_workspace_of_the_t4000_workload():
+    """The scratch holds the workspace of B=1, H 16 -> 32, dk=dv=128, chunk 64,
+    bf16 up to T=4032 and no more."""
+    lib = gdr.load_library()
+    assert gdr.binding.NOALLOC_SCRATCH_BYTES == 128 << 20
+    text = HEADER.read_text()
+    assert re.search(r"#define GDR_NOALLOC_SCRATCH_BYTES \(\(size_t\)128 << 20\)", text)
+    size = lambda T: lib.gdr_prefill_workspace_size(ctypes.byref(_big(T)), 1, 0)
+    assert size(4032) <= gdr.binding.NOALLOC_SCRATCH_BYTES < size(4033)
 
 
 def test_workspace_size_query():

@@ -8,21 +8,30 @@
 // leave the result unchanged: k = q = v = 0, beta = 0, g = 0).
 //
 // For a chunk of C tokens entered with state S (dk x dv), with
-// Gamma_r = sum_{s<=r} g_s per key channel:
-//   Kt = K e^Gamma, Kh = K e^-Gamma, Qt = Q e^Gamma
-//   A  = strict_lower(diag(beta) Kt Kh^T),   Tb = (I + A)^-1 diag(beta)
-//   P  = lower(Qt Kh^T)
+// Gamma_r = sum_{s<=r} g_s per key channel (non-increasing along the rows,
+// since g <= 0) and D_rs = e^(Gamma_r - Gamma_s) per channel:
+//   A  = strict_lower(diag(beta) (K K^T o D)),   Tb = (I + A)^-1 diag(beta)
+//   P  = lower(Q K^T o D)                        (o D: each product over
+//                                                 channel i weighted by D_rs,i)
+//   Kt = K e^Gamma, Qt = Q e^Gamma, Ke = K e^(Gamma_L - Gamma)
 //   U  = Tb (V - Kt S)                       (the WY pseudo-values minus the
 //                                             pseudo-keys applied to S)
 //   O  = scale (Qt S + P U)
-//   S' = diag(e^Gamma_L) (S + Kh^T U)
-// which is T token updates regrouped exactly (the last line is
-// diag(e^Gamma_L) S + (K e^(Gamma_L - Gamma))^T U with the decay factored out,
-// so the chunk needs no third exponential per element).
+//   S' = diag(e^Gamma_L) S + Ke^T U
+// which is C token updates regrouped exactly.  Every exponent above is <= 0
+// in the entries that are used.  How A and P are formed depends on the gate:
+//   scalar gate   D is one number per (r, s): the plain products K K^T and
+//                 Q K^T on MFMA, each entry times D_rs;
+//   channel gate  while the chunk's decay stays moderate (-Gamma_L <= 64 on
+//                 every channel), the factorised form (K e^Gamma)(K e^-Gamma)^T
+//                 on MFMA; past that, an exact routine that refers each 16x16
+//                 tile below the diagonal to the start of its row block (all
+//                 exponents <= 0, on MFMA) and sums the diagonal blocks entry
+//                 by entry.
 //
 // Kernels:
 //   chunk_prep   one workgroup per (b, h, chunk), all chunks in parallel:
-//                everything that does not depend on S -- Kt, Qt, Kh^T, Tb, P
+//                everything that does not depend on S -- Kt, Qt, Ke^T, Tb, P
 //                and e^Gamma_L -- written to the caller's workspace, one
 //                disjoint block per (b, h, chunk).
 //   chunk_carry  one workgroup per (b, h, slice of DVS state columns), walking
@@ -163,9 +172,9 @@ template <typename OpT, int DK, int C>
 struct ChunkBlock {
   static constexpr int kKt = 0;                  // [C][DK]  K e^Gamma
   static constexpr int kQt = C * DK;             // [C][DK]  Q e^Gamma
-  static constexpr int kKhT = 2 * C * DK;        // [DK][C]  (K e^-Gamma)^T
+  static constexpr int kKeT = 2 * C * DK;        // [DK][C]  (K e^(Gamma_L - Gamma))^T
   static constexpr int kTb = 3 * C * DK;         // [C][C]   (I + A)^-1 diag(beta)
-  static constexpr int kP = 3 * C * DK + C * C;  // [C][C]   lower(Qt Kh^T)
+  static constexpr int kP = 3 * C * DK + C * C;  // [C][C]   lower(Q K^T o D)
   static constexpr int kOpElems = 3 * C * DK + 2 * C * C;
   static constexpr size_t kGammaByte = static_cast<size_t>(kOpElems) * sizeof(OpT);  // [DK] f32
   static constexpr size_t kBytes = (kGammaByte + DK * sizeof(float) + 15) / 16 * 16;
@@ -179,13 +188,13 @@ struct ChunkBlock {
 //      quads of k, q, g over a part of the rows; beta once per row);
 //   2. row norms through LDS partial sums;
 //   3. per-channel prefix sums (each channel split into row parts, combined
-//      through LDS) and the decayed operands, built in fp32 and rounded once
-//      into row-major LDS;
-//   4. A and P on MFMA, computed transposed so that each lane holds four
-//      consecutive columns of a row; P leaves for the block from registers;
-//      Kt, Qt and Kh^T are copied from LDS to the block while their LDS
-//      regions are still live, consecutive threads writing consecutive lane
-//      slices (Kh^T read down the columns of Kh);
+//      through LDS);
+//   4. A and P (prep_causal_scalar, prep_causal_factored or
+//      prep_causal_exact), computed transposed so that each lane holds four
+//      consecutive columns of a row; the carry's operands Kt, Qt and Ke^T,
+//      built in fp32 and rounded once into row-major LDS, then copied to the
+//      block, consecutive threads writing consecutive lane slices (Ke^T read
+//      down the columns of Ke);
 //   5. (I + A)^-1 blocked by 16: the diagonal 16x16 blocks by forward
 //      substitution in registers (one lane per column), then the off-diagonal
 //      blocks level by level, T_ij = -T_ii sum_k A_ik T_kj, with fp32 MFMA;
@@ -199,7 +208,7 @@ __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
 
 template <typename OpT, int DK, int C>
 struct PrepSmem {
-  static constexpr int LDK = DK + pad_of<OpT>();  // rows of Kt, Kh, Qt
+  static constexpr int LDK = DK + pad_of<OpT>();  // rows of Kt, Kh, Ke, Qt
   static constexpr int LDT = C + 4;               // fp32 A (row-major), T (column-major)
   static constexpr int LDX = 20;                  // fp32 16x16 scratch of the solve
   static constexpr int NB = C / 16;
@@ -220,15 +229,21 @@ struct PrepSmem {
   static constexpr size_t kN = static_cast<size_t>(C) * LDN * sizeof(float);
   static constexpr size_t kG = static_cast<size_t>(PARTS) * DK * sizeof(float);
   // Three regions, each reused as the chunk moves on (a barrier between uses):
-  //   R0: row-norm partials -> Kt -> Qt (once A is done) -> solve scratch
-  //   R1: Kh -> T, column-major (once P is done)
+  //   R0: row-norm partials -> operand rows (Kt, Qt, K, ...) -> solve scratch
+  //   R1: operand rows (Kh, Ke, Q, ...) -> T, column-major
   //   R2: per-part channel sums of the prefix -> A
+  // (R0 + R1 also stage the exact routine's fp32 passes.)
   static constexpr size_t oR0 = 0;
   static constexpr size_t oR1 = al16(mx(mx(kOpRows, kN), kX));
   static constexpr size_t oR2 = oR1 + al16(mx(kOpRows, kTm));
   static constexpr size_t kBytes = oR2 + al16(mx(kTm, kG));
   static constexpr size_t oBeta = kBytes;  // beta of the chunk's rows
-  static constexpr size_t kAll = kBytes + al16(static_cast<size_t>(C) * sizeof(float));
+  static constexpr size_t oGam = oBeta + al16(static_cast<size_t>(C) * sizeof(float));  // scalar gate: Gamma per row
+  static constexpr size_t oNrm = oGam + al16(static_cast<size_t>(C) * sizeof(float));   // 1/|k|, 1/|q| per row
+  static constexpr size_t kAll = oNrm + al16(2 * static_cast<size_t>(C) * sizeof(float));
+  // Register arrays of a thread's channel quad over its rows.
+  using RowsF = float[RPP][4];
+  using RowsOp = OpT[RPP][4];
 };
 
 // A half-open range [n0, n1) of chunk indices.
@@ -307,6 +322,506 @@ __device__ __forceinline__ void lds_to_frag_t(OpT* region, const OpT* src, int l
   }
 }
 
+// Chunks whose largest per-channel decay over the chunk, -Gamma_L, is at most
+// this take the factorised causal terms (Kt Kh^T with Kh = K e^-Gamma, so Kh
+// is at most e^64 K and every product stays far inside fp32); chunks with a
+// stronger decay on any channel take the exact routine.
+constexpr float kFastChunkDecay = 64.0f;
+
+// A thread's rows of its channel quad (registers) to a row-major LDS buffer.
+template <typename OpT, int RPP>
+__device__ __forceinline__ void rows_to_lds(OpT* dst, int ld, int rlo, int c4,
+                                            const OpT (&v)[RPP][4]) {
+#pragma unroll
+  for (int i = 0; i < RPP; ++i) store_vec4<OpT>(dst + (rlo + i) * ld + 4 * c4, v[i]);
+}
+
+// The carry's operands Kt = K e^Gamma, Ke = K e^(Gamma_L - Gamma) and
+// Qt = Q e^Gamma, held as the thread's rows, to the block: through LDS rows
+// (R0, R1) and coalesced copies (Ke transposed).  R0 and R1 must be free on
+// entry and are free again on return.
+template <typename OpT, int DK, int C>
+__device__ __forceinline__ void emit_carry_operands(
+    const typename PrepSmem<OpT, DK, C>::RowsOp& ktr, const typename PrepSmem<OpT, DK, C>::RowsOp& ker,
+    const typename PrepSmem<OpT, DK, C>::RowsOp& qtr, int rlo, bool active, int c4, OpT* out,
+    unsigned char* sm, int tid) {
+  using Sm = PrepSmem<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C>;
+  OpT* r0 = reinterpret_cast<OpT*>(sm + Sm::oR0);
+  OpT* r1 = reinterpret_cast<OpT*>(sm + Sm::oR1);
+  if (active) {
+    rows_to_lds<OpT, Sm::RPP>(r0, Sm::LDK, rlo, c4, ktr);
+    rows_to_lds<OpT, Sm::RPP>(r1, Sm::LDK, rlo, c4, ker);
+  }
+  __syncthreads();
+  lds_to_frag<OpT, DK, C>(out + Blk::kKt, r0, Sm::LDK, tid);
+  lds_to_frag_t<OpT, C, DK>(out + Blk::kKeT, r1, Sm::LDK, tid);
+  __syncthreads();
+  if (active) rows_to_lds<OpT, Sm::RPP>(r0, Sm::LDK, rlo, c4, qtr);
+  __syncthreads();
+  lds_to_frag<OpT, DK, C>(out + Blk::kQt, r0, Sm::LDK, tid);
+  __syncthreads();
+}
+
+// Row and column of lower-triangular 16x16 tile `job` (row-major order over
+// the tiles with S <= R).
+__device__ __forceinline__ void lower_tile(int job, int& R, int& S) {
+  R = 0;
+  while ((R + 1) * (R + 2) / 2 <= job) ++R;
+  S = job - R * (R + 1) / 2;
+}
+
+// Causal terms for a scalar gate (one decay per row): the decays leave the
+// contraction, so A and P come from the plain products K K^T and Q K^T on
+// MFMA, each entry scaled by e^(Gamma_r - Gamma_s) <= 1 -- exact for any
+// decay.  Kt, Ke and Qt are per-row scalings with exponents <= 0.
+template <typename OpT, int DK, int C>
+__device__ __forceinline__ void prep_causal_scalar(
+    const typename PrepSmem<OpT, DK, C>::RowsF& kq, const typename PrepSmem<OpT, DK, C>::RowsF& qq,
+    const typename PrepSmem<OpT, DK, C>::RowsF& gq, float gam0, float total, int rlo, bool active,
+    int c4, OpT* out, unsigned char* sm, int tid, int lane, int wave) {
+  using Sm = PrepSmem<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C>;
+  constexpr int LDK = Sm::LDK, LDT = Sm::LDT, NB = Sm::NB, RPP = Sm::RPP;
+  OpT* Kr_s = reinterpret_cast<OpT*>(sm + Sm::oR0);  // K rows as given
+  OpT* Qr_s = reinterpret_cast<OpT*>(sm + Sm::oR1);  // Q rows as given
+  float* A_s = reinterpret_cast<float*>(sm + Sm::oR2);
+  float* gam_s = reinterpret_cast<float*>(sm + Sm::oGam);
+  const float* beta_s = reinterpret_cast<const float*>(sm + Sm::oBeta);
+
+  OpT ktr[RPP][4], ker[RPP][4], qtr[RPP][4];
+  if (active) {
+    float gam = gam0;
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+      const int r = rlo + i;
+      gam += gq[i][0];
+      const float ep = __builtin_amdgcn_exp2f(gam * kLog2e);
+      const float ef = __builtin_amdgcn_exp2f((total - gam) * kLog2e);
+      OpT kr[4], qr[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kr[u] = from_f32<OpT>(kq[i][u]);
+        qr[u] = from_f32<OpT>(qq[i][u]);
+        ktr[i][u] = from_f32<OpT>(kq[i][u] * ep);
+        ker[i][u] = from_f32<OpT>(kq[i][u] * ef);
+        qtr[i][u] = from_f32<OpT>(qq[i][u] * ep);
+      }
+      store_vec4<OpT>(Kr_s + r * LDK + 4 * c4, kr);
+      store_vec4<OpT>(Qr_s + r * LDK + 4 * c4, qr);
+      if (c4 == 0) gam_s[r] = gam;
+    }
+  }
+  __syncthreads();
+
+  // Lower tiles: A and P of a tile by one wave, computed transposed (each
+  // lane holds four consecutive columns of one row) with one shared decay
+  // factor per entry; tiles above the diagonal of P are zeros.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int NL = NB * (NB + 1) / 2;
+  for (int job = wv; job < NL; job += kThreads / 64) {
+    int R, S;
+    lower_tile(job, R, S);
+    f32x4 ga = {0.f, 0.f, 0.f, 0.f}, gp = {0.f, 0.f, 0.f, 0.f};
+    ga = mma_xzt<OpT, DK>(Kr_s, LDK, 16 * S, Kr_s, LDK, 16 * R, ga, lane);
+    gp = mma_xzt<OpT, DK>(Kr_s, LDK, 16 * S, Qr_s, LDK, 16 * R, gp, lane);
+    const int row = 16 * R + (lane & 15);
+    const int col = 16 * S + 4 * (lane >> 4);
+    const float gr = gam_s[row], br = beta_s[row];
+    float av[4];
+    OpT pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = col + e;
+      const float f = row >= c ? __builtin_amdgcn_exp2f((gr - gam_s[c]) * kLog2e) : 0.0f;
+      av[e] = row > c ? br * f * ga[e] : 0.0f;
+      pv[e] = from_f32<OpT>(f * gp[e]);
+    }
+    *reinterpret_cast<float4*>(A_s + row * LDT + col) = make_float4(av[0], av[1], av[2], av[3]);
+    frag_store<OpT, C, 4>(out + Blk::kP, row, col, pv);
+  }
+  for (int job = wv; job < NB * NB; job += kThreads / 64) {
+    const int R = job / NB, S = job % NB;
+    if (S > R) {
+      const OpT z[4] = {from_f32<OpT>(0.f), from_f32<OpT>(0.f), from_f32<OpT>(0.f),
+                        from_f32<OpT>(0.f)};
+      frag_store<OpT, C, 4>(out + Blk::kP, 16 * R + (lane & 15), 16 * S + 4 * (lane >> 4), z);
+    }
+  }
+  __syncthreads();  // K and Q rows are dead
+  emit_carry_operands<OpT, DK, C>(ktr, ker, qtr, rlo, active, c4, out, sm, tid);
+}
+
+// Causal terms for a channel gate whose chunk decays by at most
+// kFastChunkDecay on every channel: factorised as Kt Kh^T and Qt Kh^T with
+// Kt = K e^Gamma, Qt = Q e^Gamma and Kh = K e^-Gamma, two exponentials per
+// key element.  Kt goes to LDS for A and to the block; Qt replaces it for P;
+// Ke = Kh e^Gamma_L replaces Kh once P is done.  `strong`: this thread's
+// channels decay by more over the chunk.  The workgroup votes at the barrier
+// after the operand rows; if any thread is strong the routine stops there
+// (the rows only went to LDS) and returns false: the chunk is then left to
+// prep_causal_exact.
+template <typename OpT, int DK, int C>
+__device__ __forceinline__ bool prep_causal_factored(
+    const typename PrepSmem<OpT, DK, C>::RowsF& kq, const typename PrepSmem<OpT, DK, C>::RowsF& qq,
+    const typename PrepSmem<OpT, DK, C>::RowsF& gq, const float (&gam0)[4],
+    const float (&total)[4], bool strong, int rlo, bool active, int c4, OpT* out,
+    unsigned char* sm, int tid, int lane, int wave) {
+  using Sm = PrepSmem<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C>;
+  constexpr int LDK = Sm::LDK, LDT = Sm::LDT, NB = Sm::NB, RPP = Sm::RPP;
+  OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);
+  OpT* Qt_s = Kt_s;  // once A is done
+  OpT* Kh_s = reinterpret_cast<OpT*>(sm + Sm::oR1);
+  OpT* Ke_s = Kh_s;  // once P is done
+  float* A_s = reinterpret_cast<float*>(sm + Sm::oR2);
+  const float* beta_s = reinterpret_cast<const float*>(sm + Sm::oBeta);
+
+  OpT qtr[RPP][4], ker[RPP][4];
+  if (active) {
+    float eL[4], gam[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      eL[u] = __builtin_amdgcn_exp2f(total[u] * kLog2e);
+      gam[u] = gam0[u];
+    }
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+      const int r = rlo + i;
+      OpT kt[4], kh[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        gam[u] += gq[i][u];
+        // e^(+-x) as 2^(+-x log2 e): one scaling serves both signs.
+        const float x = gam[u] * kLog2e;
+        const float e_pos = __builtin_amdgcn_exp2f(x), e_neg = __builtin_amdgcn_exp2f(-x);
+        kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
+        kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
+        qtr[i][u] = from_f32<OpT>(qq[i][u] * e_pos);
+        ker[i][u] = from_f32<OpT>(kq[i][u] * (e_neg * eL[u]));
+      }
+      store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
+      store_vec4<OpT>(Kh_s + r * LDK + 4 * c4, kh);
+    }
+  }
+  // The vote is the barrier; readfirstlane tells the compiler that its
+  // result is the same in every lane (so that the two routines sit on the
+  // two sides of a plain branch, not in sequence).
+  if (__builtin_amdgcn_readfirstlane(__syncthreads_or(strong)) != 0) return false;
+
+  // A = strict_lower(diag(beta) Kt Kh^T), one lower 16x16 tile per job,
+  // computed transposed (Kh Kt^T): each lane then holds four consecutive
+  // columns of one row of A, one 16-byte LDS store.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // jobs are wave-uniform
+  constexpr int NL = NB * (NB + 1) / 2;
+  for (int job = wv; job < NL; job += kThreads / 64) {
+    int R, S;
+    lower_tile(job, R, S);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mma_xzt<OpT, DK>(Kh_s, LDK, 16 * S, Kt_s, LDK, 16 * R, acc, lane);
+    const int row = 16 * R + (lane & 15);
+    const int col = 16 * S + 4 * (lane >> 4);
+    const float br = beta_s[row];
+    *reinterpret_cast<float4*>(A_s + row * LDT + col) =
+        make_float4(row > col ? br * acc[0] : 0.0f, row > col + 1 ? br * acc[1] : 0.0f,
+                    row > col + 2 ? br * acc[2] : 0.0f, row > col + 3 ? br * acc[3] : 0.0f);
+  }
+  lds_to_frag<OpT, DK, C>(out + Blk::kKt, Kt_s, LDK, tid);
+  __syncthreads();  // Kt is dead: its storage takes Qt
+  if (active) rows_to_lds<OpT, RPP>(Qt_s, LDK, rlo, c4, qtr);
+  __syncthreads();
+
+  // P = lower(Qt Kh^T), transposed like A, straight to the block in fragment
+  // order; tiles above the diagonal are written as zeros.
+  for (int job = wv; job < NB * NB; job += kThreads / 64) {
+    const int R = job / NB, S = job % NB;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (S <= R) acc = mma_xzt<OpT, DK>(Kh_s, LDK, 16 * S, Qt_s, LDK, 16 * R, acc, lane);
+    const int row = 16 * R + (lane & 15);
+    const int col = 16 * S + 4 * (lane >> 4);
+    OpT v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = from_f32<OpT>(row >= col + e ? acc[e] : 0.0f);
+    frag_store<OpT, C, 4>(out + Blk::kP, row, col, v);
+  }
+  lds_to_frag<OpT, DK, C>(out + Blk::kQt, Qt_s, LDK, tid);
+  __syncthreads();  // Kh and Qt are dead: Ke takes Kh's storage
+  if (active) rows_to_lds<OpT, RPP>(Ke_s, LDK, rlo, c4, ker);
+  __syncthreads();
+  lds_to_frag_t<OpT, C, DK>(out + Blk::kKeT, Ke_s, LDK, tid);
+  __syncthreads();
+  return true;
+}
+
+// Staging of the exact routine: the channels go in passes of KP, each pass
+// holding K, Q and Gamma of every row of the chunk in fp32 LDS (R0 + R1).
+template <typename OpT, int DK, int C>
+struct ExactPass {
+  using Sm = PrepSmem<OpT, DK, C>;
+  static constexpr bool fits(int kp) { return 3 * C * (kp + 4) * 4 <= static_cast<int>(Sm::oR2); }
+  static constexpr int KP = DK < 32 ? DK : (fits(32) ? 32 : 16);
+  static constexpr int LDP = KP + 4;
+  static constexpr int NPASS = DK / KP;
+  static constexpr int NB = C / 16;
+  static constexpr int NOFF = NB * (NB - 1) / 2;              // tiles below the diagonal
+  static constexpr int JPW = NOFF > 0 ? (NOFF + 3) / 4 : 1;    // of them per wave
+  static constexpr int NDE = NB * 136;                          // diagonal-block entries, r >= s
+  static constexpr int EPT = (NDE + kThreads - 1) / kThreads;   // of them per thread
+  static constexpr int LDPB = C + pad_of<OpT>();                // P staged row-major in LDS
+  static_assert(fits(KP), "pass staging fits R0 + R1");
+  static_assert(static_cast<size_t>(C) * LDPB * sizeof(OpT) <= Sm::oR2, "P staging fits R0 + R1");
+  static_assert(KP % 4 == 0 && DK % KP == 0, "pass width");
+};
+
+// The lane's MFMA fragment (contraction over a pass's KP channels) of the 16
+// rows row0 ... row0 + 15: X[row][ch] e^(sgn (G[row][ch] - E[ch])), where E
+// is the reference row of Gamma; sgn = +1 for rows at or after the reference
+// row, -1 for rows at or before it, so that the exponent is <= 0.  With two
+// sources the exponential is shared.
+template <typename OpT, int KP, int LDP, int NSRC>
+__device__ __forceinline__ void exact_frags(const float* X0, const float* X1, const float* G,
+                                            const float* E, int row0, int step, int lane,
+                                            float sgn, typename FragT<OpT, KP>::T (&f)[NSRC]) {
+  using F = FragT<OpT, KP>;
+  const int row = row0 + (lane & 15);
+  const int ch0 = step * F::KS + (lane >> 4) * F::VL;
+  OpT v0[F::VL], v1[F::VL];
+#pragma unroll
+  for (int j = 0; j < F::VL; ++j) {
+    const int ch = ch0 + j;
+    const float d = __builtin_amdgcn_exp2f(sgn * (G[row * LDP + ch] - E[ch]) * kLog2e);
+    v0[j] = from_f32<OpT>(X0[row * LDP + ch] * d);
+    if constexpr (NSRC > 1) v1[j] = from_f32<OpT>(X1[row * LDP + ch] * d);
+  }
+  __builtin_memcpy(&f[0], v0, sizeof(f[0]));
+  if constexpr (NSRC > 1) __builtin_memcpy(&f[1], v1, sizeof(f[1]));
+}
+
+// Entry `idx` (< NB * 136) of the diagonal 16x16 blocks, r >= s, as absolute
+// chunk rows.
+__device__ __forceinline__ void diag_entry(int idx, int& r, int& s) {
+  const int blk = idx / 136, loc = idx % 136;
+  int rl = 0;
+  while ((rl + 1) * (rl + 2) / 2 <= loc) ++rl;
+  r = 16 * blk + rl;
+  s = 16 * blk + loc - rl * (rl + 1) / 2;
+}
+
+// k, q (normalised with the 1/norms in nrm_s, io dtype widened to fp32) and
+// g of the thread's channel quad at chunk row r, read again from the inputs;
+// zero past the chunk's end.
+template <typename OpT, int DK>
+__device__ __forceinline__ void reload_quad_row(const PrefillArgs& a, size_t qk_row0,
+                                                size_t g_row0, int L, int r, int c4, bool live,
+                                                const float* nrm_s, float (&k4)[4],
+                                                float (&q4)[4], float (&g4)[4]) {
+  const int rr = min(r, L - 1);
+  const size_t off = (qk_row0 + static_cast<size_t>(rr) * a.H_qk) * DK + 4 * c4;
+  load_row<OpT, 4>(static_cast<const OpT*>(a.k) + off, k4);
+  load_row<OpT, 4>(static_cast<const OpT*>(a.q) + off, q4);
+  const size_t gi = g_row0 + static_cast<size_t>(rr) * a.H_v;
+  load_row<float, 4>(a.gate_in + gi * DK + 4 * c4, g4);
+  live = live && r < L;
+  const float nk = live ? nrm_s[2 * r] : 0.0f, nq = live ? nrm_s[2 * r + 1] : 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    k4[u] *= nk;
+    q4[u] *= nq;
+    g4[u] = live ? g4[u] : 0.0f;
+  }
+}
+
+// Causal terms for a channel gate with a strong decay somewhere in the chunk:
+// exact, with every exponent <= 0.  Per pass of KP channels (fp32 K, Q and
+// Gamma of all rows staged in LDS by the threads whose channel quads lie in
+// the pass, read again from the inputs so that nothing of the chunk is held
+// in registers across the passes):
+//   - the tiles below the diagonal, (R, S < R), on MFMA, referred to the end
+//     of row block R - 1: E = Gamma at row 16R - 1, rows r of block R scaled
+//     by e^(Gamma_r - E) and rows s < 16R by e^(E - Gamma_s);
+//   - the diagonal 16x16 blocks entry by entry, with e^(Gamma_r - Gamma_s).
+// A and P are accumulated over the passes in registers, then written to A_s
+// and, through a row-major LDS tile, to the block.
+template <typename OpT, int DK, int C>
+__device__ __forceinline__ void prep_causal_exact(const PrefillArgs& a, size_t qk_row0,
+                                                  size_t g_row0, int L, const float (&gam0)[4],
+                                                  const float (&total)[4], int rlo, bool active,
+                                                  int c4, OpT* out, unsigned char* sm, int tid,
+                                                  int lane, int wave) {
+  using Sm = PrepSmem<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C>;
+  using X = ExactPass<OpT, DK, C>;
+  using F = FragT<OpT, X::KP>;
+  constexpr int LDT = Sm::LDT, RPP = Sm::RPP, KP = X::KP, LDP = X::LDP;
+  float* Kp = reinterpret_cast<float*>(sm + Sm::oR0);  // [C][LDP] per pass
+  float* Qp = Kp + C * LDP;
+  float* Gp = Qp + C * LDP;
+  float* A_s = reinterpret_cast<float*>(sm + Sm::oR2);
+  const float* beta_s = reinterpret_cast<const float*>(sm + Sm::oBeta);
+  const float* nrm_s = reinterpret_cast<const float*>(sm + Sm::oNrm);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+  f32x4 accA[X::JPW], accP[X::JPW];
+#pragma unroll
+  for (int j = 0; j < X::JPW; ++j) accA[j] = accP[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dA[X::EPT], dP[X::EPT];
+#pragma unroll
+  for (int e = 0; e < X::EPT; ++e) dA[e] = dP[e] = 0.0f;
+
+#pragma unroll 1
+  for (int pass = 0; pass < X::NPASS; ++pass) {
+    // the threads whose channel quad lies in this pass stage their rows
+    if (active && (4 * c4) / KP == pass) {
+      const int cc = 4 * c4 - pass * KP;
+      float g[4] = {gam0[0], gam0[1], gam0[2], gam0[3]};
+#pragma unroll 2
+      for (int i = 0; i < RPP; ++i) {
+        const int r = rlo + i;
+        float k4[4], q4[4], g4[4];
+        reload_quad_row<OpT, DK>(a, qk_row0, g_row0, L, r, c4, true, nrm_s, k4, q4, g4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) g[u] += g4[u];
+        *reinterpret_cast<float4*>(Kp + r * LDP + cc) = make_float4(k4[0], k4[1], k4[2], k4[3]);
+        *reinterpret_cast<float4*>(Qp + r * LDP + cc) = make_float4(q4[0], q4[1], q4[2], q4[3]);
+        *reinterpret_cast<float4*>(Gp + r * LDP + cc) = make_float4(g[0], g[1], g[2], g[3]);
+      }
+    }
+    __syncthreads();
+    // tiles below the diagonal, computed transposed as in the other routines
+#pragma unroll
+    for (int j = 0; j < X::JPW; ++j) {
+      const int job = wv + j * (kThreads / 64);
+      if (job < X::NOFF) {
+        int R = 1, S = job;
+        while (S >= R) {
+          S -= R;
+          ++R;
+        }
+        const float* E = Gp + (16 * R - 1) * LDP;
+#pragma unroll
+        for (int st = 0; st < F::STEPS; ++st) {
+          typename F::T zc[1], zr[2];
+          exact_frags<OpT, KP, LDP, 1>(Kp, nullptr, Gp, E, 16 * S, st, lane, -1.0f, zc);
+          exact_frags<OpT, KP, LDP, 2>(Kp, Qp, Gp, E, 16 * R, st, lane, 1.0f, zr);
+          accA[j] = F::mma(zc[0], zr[0], accA[j]);
+          accP[j] = F::mma(zc[0], zr[1], accP[j]);
+        }
+      }
+    }
+    // diagonal blocks, entry by entry
+#pragma unroll
+    for (int e = 0; e < X::EPT; ++e) {
+      const int idx = tid + e * kThreads;
+      if (idx < X::NDE) {
+        int r, s;
+        diag_entry(idx, r, s);
+        float sa = 0.f, sp = 0.f;
+#pragma unroll 2
+        for (int ch = 0; ch < KP; ch += 4) {
+          const float4 kr = *reinterpret_cast<const float4*>(Kp + r * LDP + ch);
+          const float4 qr = *reinterpret_cast<const float4*>(Qp + r * LDP + ch);
+          const float4 gr = *reinterpret_cast<const float4*>(Gp + r * LDP + ch);
+          const float4 ks = *reinterpret_cast<const float4*>(Kp + s * LDP + ch);
+          const float4 gs = *reinterpret_cast<const float4*>(Gp + s * LDP + ch);
+          const float kra[4] = {kr.x, kr.y, kr.z, kr.w}, qra[4] = {qr.x, qr.y, qr.z, qr.w};
+          const float gra[4] = {gr.x, gr.y, gr.z, gr.w}, ksa[4] = {ks.x, ks.y, ks.z, ks.w};
+          const float gsa[4] = {gs.x, gs.y, gs.z, gs.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float t = ksa[u] * __builtin_amdgcn_exp2f((gra[u] - gsa[u]) * kLog2e);
+            sa += kra[u] * t;
+            sp += qra[u] * t;
+          }
+        }
+        dA[e] += sa;
+        dP[e] += sp;
+      }
+    }
+    __syncthreads();  // the next pass overwrites the staging
+  }
+
+  // A to A_s (times beta of the row, strictly below the diagonal); P row-major
+  // into LDS (zeros above the diagonal), then to the block in fragment order.
+  OpT* Pb = reinterpret_cast<OpT*>(sm + Sm::oR0);
+  for (int i = tid; i < C * C; i += kThreads) {
+    const int r = i / C, c = i % C;
+    if (c > r) {
+      Pb[r * X::LDPB + c] = from_f32<OpT>(0.0f);
+      if (c / 16 == r / 16) A_s[r * LDT + c] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < X::JPW; ++j) {
+    const int job = wv + j * (kThreads / 64);
+    if (job < X::NOFF) {
+      int R = 1, S = job;
+      while (S >= R) {
+        S -= R;
+        ++R;
+      }
+      const int row = 16 * R + (lane & 15);
+      const int col = 16 * S + 4 * (lane >> 4);
+      const float br = beta_s[row];
+      *reinterpret_cast<float4*>(A_s + row * LDT + col) =
+          make_float4(br * accA[j][0], br * accA[j][1], br * accA[j][2], br * accA[j][3]);
+      const OpT pv[4] = {from_f32<OpT>(accP[j][0]), from_f32<OpT>(accP[j][1]),
+                         from_f32<OpT>(accP[j][2]), from_f32<OpT>(accP[j][3])};
+      store_vec4<OpT>(Pb + row * X::LDPB + col, pv);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < X::EPT; ++e) {
+    const int idx = tid + e * kThreads;
+    if (idx < X::NDE) {
+      int r, s;
+      diag_entry(idx, r, s);
+      A_s[r * LDT + s] = r > s ? beta_s[r] * dA[e] : 0.0f;
+      Pb[r * X::LDPB + s] = from_f32<OpT>(dP[e]);
+    }
+  }
+  __syncthreads();
+  lds_to_frag<OpT, C, C>(out + Blk::kP, Pb, X::LDPB, tid);
+  __syncthreads();
+
+  // Kt, Ke and Qt: exponents Gamma and Gamma_L - Gamma, both <= 0.  Kt and
+  // Ke rows go to LDS row by row; Qt waits in registers.
+  constexpr int LDK = Sm::LDK;
+  OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);
+  OpT* Ke_s = reinterpret_cast<OpT*>(sm + Sm::oR1);
+  OpT qtr[RPP][4];
+  if (active) {
+    float g[4] = {gam0[0], gam0[1], gam0[2], gam0[3]};
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+      const int r = rlo + i;
+      float k4[4], q4[4], g4[4];
+      reload_quad_row<OpT, DK>(a, qk_row0, g_row0, L, r, c4, true, nrm_s, k4, q4, g4);
+      OpT kt[4], ke[4], qt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        g[u] += g4[u];
+        const float ep = __builtin_amdgcn_exp2f(g[u] * kLog2e);
+        const float ef = __builtin_amdgcn_exp2f((total[u] - g[u]) * kLog2e);
+        kt[u] = from_f32<OpT>(k4[u] * ep);
+        ke[u] = from_f32<OpT>(k4[u] * ef);
+        qt[u] = from_f32<OpT>(q4[u] * ep);
+      }
+      store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
+      store_vec4<OpT>(Ke_s + r * LDK + 4 * c4, ke);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) qtr[i][u] = qt[u];
+    }
+  }
+  __syncthreads();
+  lds_to_frag<OpT, DK, C>(out + Blk::kKt, Kt_s, LDK, tid);
+  lds_to_frag_t<OpT, C, DK>(out + Blk::kKeT, Ke_s, LDK, tid);
+  __syncthreads();
+  if (active) rows_to_lds<OpT, RPP>(Kt_s, LDK, rlo, c4, qtr);
+  __syncthreads();
+  lds_to_frag<OpT, DK, C>(out + Blk::kQt, Kt_s, LDK, tid);
+  __syncthreads();
+}
+
 // kChannel: per-channel log-decays (one per key channel and row); otherwise one
 // per row (plain or fused), broadcast over the channels.
 // One work unit (b, h, chunk) per workgroup, over the chunks of cr; wg is the
@@ -316,15 +831,12 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
                                           unsigned char* sm) {
   using Sm = PrepSmem<OpT, DK, C>;
   using Blk = ChunkBlock<OpT, DK, C>;
-  constexpr int LDK = Sm::LDK, LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
+  constexpr int LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
   constexpr int PARTS = Sm::PARTS, RPP = Sm::RPP;
 
   float* beta_s = reinterpret_cast<float*>(sm + Sm::oBeta);
 
-  OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);
-  OpT* Qt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);     // after A
-  float* X_s = reinterpret_cast<float*>(sm + Sm::oR0);  // after P
-  OpT* Kh_s = reinterpret_cast<OpT*>(sm + Sm::oR1);
+  float* X_s = reinterpret_cast<float*>(sm + Sm::oR0);   // solve scratch
   float* TT_s = reinterpret_cast<float*>(sm + Sm::oR1);  // T column-major: TT[s][r] = T[r][s]
   float* gpart = reinterpret_cast<float*>(sm + Sm::oR2); // [PARTS][DK]
   float* A_s = reinterpret_cast<float*>(sm + Sm::oR2);   // A row-major
@@ -414,6 +926,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
   // ---- 2. row L2 norms: each thread leaves its quad's partial sums in LDS,
   //         one thread per row adds them up ----
   float* nrm = reinterpret_cast<float*>(sm + Sm::oR0);  // [C][2 NQ + 1] partials, then 1/norms
+  float* nrm_s = reinterpret_cast<float*>(sm + Sm::oNrm);
+  if (kChannel && !a.l2norm && tid < C) {
+    nrm_s[2 * tid] = 1.0f;
+    nrm_s[2 * tid + 1] = 1.0f;
+  }
   if (a.l2norm) {
     if (active) {
 #pragma unroll
@@ -437,6 +954,10 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
       }
       nrm[tid * Sm::LDN] = 1.0f / sqrtf(sk + kL2Eps);
       nrm[tid * Sm::LDN + 1] = 1.0f / sqrtf(sq + kL2Eps);
+      if constexpr (kChannel) {  // kept for the exact routine, which reads k and q again
+        nrm_s[2 * tid] = nrm[tid * Sm::LDN];
+        nrm_s[2 * tid + 1] = nrm[tid * Sm::LDN + 1];
+      }
     }
     __syncthreads();
     if (active) {
@@ -452,13 +973,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
     }
   }
 
-  // ---- 3. per-channel prefix sums and decayed operands ----
-  // Kt and Kh go to LDS for A and P.  Kt, Qt and Kh^T also go from registers
-  // straight to the block in fragment order; Qt stays in registers until
-  // Kt's storage is free.
+  // ---- 3. per-channel prefix sums: each channel's rows are split into
+  //         parts, whose sums are combined through LDS.  gam0: Gamma just
+  //         before row rlo; total: Gamma_L, per channel of the thread's quad ----
   OpT* out = reinterpret_cast<OpT*>(blk_bytes);
-  OpT qtr[RPP][4];
-  float gam[4] = {0.f, 0.f, 0.f, 0.f}, total[4] = {0.f, 0.f, 0.f, 0.f};
+  float gam0[4] = {0.f, 0.f, 0.f, 0.f}, total[4] = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -474,96 +993,33 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
       const float xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (p < part) gam[u] += xv[u];
+        if (p < part) gam0[u] += xv[u];
         total[u] += xv[u];
       }
-    }
-    // gam: Gamma just before row rlo; total: Gamma_L, per channel of the quad.
-#pragma unroll
-    for (int i = 0; i < RPP; ++i) {
-      const int r = rlo + i;
-      OpT kt[4], kh[4];
-      float ep[4], en[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) gam[u] += gq[i][u];
-      // e^(+-x) as 2^(+-x log2 e): one scaling serves both signs (the same
-      // values as two fast exponentials, since negation is exact).
-      if constexpr (kChannel) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float x = gam[u] * kLog2e;
-          ep[u] = __builtin_amdgcn_exp2f(x);
-          en[u] = __builtin_amdgcn_exp2f(-x);
-        }
-      } else {
-        // One decay per row: the four prefix sums are the same operations on
-        // the same values, so one pair of exponentials serves the quad.
-        const float x = gam[0] * kLog2e;
-        const float p = __builtin_amdgcn_exp2f(x), n = __builtin_amdgcn_exp2f(-x);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ep[u] = p;
-          en[u] = n;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float e_pos = ep[u], e_neg = en[u];
-        kt[u] = from_f32<OpT>(kq[i][u] * e_pos);
-        kh[u] = from_f32<OpT>(kq[i][u] * e_neg);
-        qtr[i][u] = from_f32<OpT>(qq[i][u] * e_pos);
-      }
-      store_vec4<OpT>(Kt_s + r * LDK + 4 * c4, kt);
-      store_vec4<OpT>(Kh_s + r * LDK + 4 * c4, kh);
     }
     if (part == 0)
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(blk_bytes + Blk::kGammaByte) + 4 * c4) =
           make_float4(expf(total[0]), expf(total[1]), expf(total[2]), expf(total[3]));
   }
-  __syncthreads();
 
-  // ---- 4a. A = strict_lower(diag(beta) Kt Kh^T), one lower 16x16 tile per
-  //          job, computed transposed (Kh Kt^T): each lane then holds four
-  //          consecutive columns of one row of A, one 16-byte LDS store ----
-  const int wv = __builtin_amdgcn_readfirstlane(wave);  // jobs are wave-uniform
-  constexpr int NL = NB * (NB + 1) / 2;
-  for (int job = wv; job < NL; job += kThreads / 64) {
-    int R = 0;
-    while ((R + 1) * (R + 2) / 2 <= job) ++R;
-    const int S = job - R * (R + 1) / 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mma_xzt<OpT, DK>(Kh_s, LDK, 16 * S, Kt_s, LDK, 16 * R, acc, lane);
-    const int row = 16 * R + (lane & 15);
-    const int col = 16 * S + 4 * (lane >> 4);
-    const float br = beta_s[row];
-    *reinterpret_cast<float4*>(A_s + row * LDT + col) =
-        make_float4(row > col ? br * acc[0] : 0.0f, row > col + 1 ? br * acc[1] : 0.0f,
-                    row > col + 2 ? br * acc[2] : 0.0f, row > col + 3 ? br * acc[3] : 0.0f);
-  }
-  lds_to_frag<OpT, DK, C>(out + Blk::kKt, Kt_s, LDK, tid);
-  __syncthreads();  // Kt is dead: its storage takes Qt
-  if (active) {
+  // ---- 4. the causal terms A = strict_lower(diag(beta) (K K^T o D)) and
+  //         P = lower(Q K^T o D), D_rs = e^(Gamma_r - Gamma_s) per channel,
+  //         into A_s (fp32) and the block; and the carry's operands Kt, Qt,
+  //         Ke^T into the block.  Every exponent that these need is <= 0
+  //         (Gamma falls along the rows) except in the factorised form, which
+  //         is used only where its e^-Gamma stays small ----
+  if constexpr (!kChannel) {
+    prep_causal_scalar<OpT, DK, C>(kq, qq, gq, gam0[0], total[0], rlo, active, c4, out, sm, tid,
+                                   lane, wave);
+  } else {
+    bool strong = false;
 #pragma unroll
-    for (int i = 0; i < RPP; ++i) store_vec4<OpT>(Qt_s + (rlo + i) * LDK + 4 * c4, qtr[i]);
+    for (int u = 0; u < 4; ++u) strong |= active && -total[u] > kFastChunkDecay;
+    if (!prep_causal_factored<OpT, DK, C>(kq, qq, gq, gam0, total, strong, rlo, active, c4, out,
+                                          sm, tid, lane, wave))
+      prep_causal_exact<OpT, DK, C>(a, qk_row0, g_row0, L, gam0, total, rlo, active, c4, out, sm,
+                                    tid, lane, wave);
   }
-  __syncthreads();
-
-  // ---- 4b. P = lower(Qt Kh^T), transposed like A, straight to the block in
-  //          fragment order; tiles above the diagonal are written as zeros ----
-  for (int job = wv; job < NB * NB; job += kThreads / 64) {
-    const int R = job / NB, S = job % NB;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (S <= R) acc = mma_xzt<OpT, DK>(Kh_s, LDK, 16 * S, Qt_s, LDK, 16 * R, acc, lane);
-    const int row = 16 * R + (lane & 15);
-    const int col = 16 * S + 4 * (lane >> 4);
-    OpT v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = from_f32<OpT>(row >= col + e ? acc[e] : 0.0f);
-    frag_store<OpT, C, 4>(out + Blk::kP, row, col, v);
-  }
-  lds_to_frag<OpT, DK, C>(out + Blk::kQt, Qt_s, LDK, tid);
-  lds_to_frag_t<OpT, C, DK>(out + Blk::kKhT, Kh_s, LDK, tid);
-  __syncthreads();  // Kh and Qt are dead: their storage takes T and the solve scratch
 
   // ---- 5a. diagonal 16x16 blocks of (I + A)^-1: lane = column ----
   // x_r = -sum_{m<r} A_rm x_m, with four independent partial sums per row
@@ -670,7 +1126,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, Chu
 //   [B1]  S^T (operand type) written
 //   c:    R = V - Kt S (to LDS, transposed), O = Qt S (registers)      [B2]
 //   d:    U = Tb R (to LDS, transposed)                                  [B3]
-//   e:    O += P U -> o;  S = e^Gamma_L . (S + Kh^T U)
+//   e:    O += P U -> o;  S = e^Gamma_L . S + Ke^T U
 // ---------------------------------------------------------------------------
 
 
@@ -725,13 +1181,13 @@ struct CarryFrags {
   using Sh = CarryShape<OpT, DK, DVS, C>;
   typename Sh::FK::T kt[Sh::OPW][Sh::FK::STEPS], qt[Sh::OPW][Sh::FK::STEPS];
   typename Sh::FC::T tb[Sh::OPW][Sh::FC::STEPS], p[Sh::OPW][Sh::FC::STEPS];
-  typename Sh::FC::T kh[Sh::SPW][Sh::FC::STEPS];
+  typename Sh::FC::T ke[Sh::SPW][Sh::FC::STEPS];
   float v[Sh::OPW][4];
   float gam[Sh::SPW][4];
 };
 
 // Issue the loads of chunk nn's fragments for this wave's tiles, by phase:
-// phase c needs Kt, Qt and V; phase d Tb; phase e P, Kh^T and e^Gamma_L.
+// phase c needs Kt, Qt and V; phase d Tb; phase e P, Ke^T and e^Gamma_L.
 template <typename OpT, int DK, int DVS, int C, int PHASE, int MODE>
 __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
                                            const unsigned char* ws_head, int nn, int b, int h,
@@ -792,7 +1248,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
         const int I = t / Sh::DVT;
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s)
-          F.kh[j][s] = FC::load(blk + Blk::kKhT, 16 * I, s, lane);
+          F.ke[j][s] = FC::load(blk + Blk::kKeT, 16 * I, s, lane);
         const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
         F.gam[j][0] = g4.x;
         F.gam[j][1] = g4.y;
@@ -1016,20 +1472,22 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
         }
       }
     }
-    // S = diag(e^Gamma_L) (S + Kh^T U).
+    // S = diag(e^Gamma_L) S + Ke^T U.
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = wave * SPW + i;
       if (NST % Sh::NW == 0 || t < NST) {
         const int I = t / DVT, J = t % DVT;
+        // Ke^T U from zero, so that the products do not wait for the decay.
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s) {
-          sacc[i] = FC::mma(F.kh[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), sacc[i]);
-          F.kh[i][s] = FC::load(nblk + Blk::kKhT, 16 * I, s, lane);
+          t = FC::mma(F.ke[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), t);
+          F.ke[i][s] = FC::load(nblk + Blk::kKeT, 16 * I, s, lane);
           pin_order<Sh::kPinLoads>();
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[i][e] *= F.gam[i][e];
+        for (int e = 0; e < 4; ++e) sacc[i][e] = F.gam[i][e] * sacc[i][e] + t[e];
         carry_load_gam<OpT, DK, DVS, C>(F, nblk, i, I, lane);
       }
     }
@@ -1383,13 +1841,26 @@ SegPlan carry_segments(int B, int T, int H_v, int dk, int dv, int chunk) {
 }
 
 // Bytes of the segmented carry's buffers (S and N: [P][units][dk][dv],
-// M: [P][units][dk][dk], fp32), placed after the chunk blocks.
+// M: [P][units][dk][dk], fp32).
 size_t seg_bytes(SegPlan sp, long units, int dk, int dv) {
   if (sp.P < 3) return 0;
   return static_cast<size_t>(sp.P) * units * dk * (2 * static_cast<size_t>(dv) + dk) *
          sizeof(float);
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout: the chunk blocks ((b, h)-major, then chunk); at the next
+// 256-byte boundary, the segmented carry's buffers (if it runs).
+struct WsLayout {
+  size_t seg, total;
+};
+WsLayout ws_layout(long units, size_t nc, size_t block_bytes, size_t seg) {
+  const size_t blocks = static_cast<size_t>(units) * nc * block_bytes;
+  WsLayout w;
+  w.seg = align256(blocks);
+  w.total = seg ? w.seg + seg : blocks;
+  return w;
+}
 
 template <typename OpT, int DK, int C>
 hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t stream) {
@@ -1398,9 +1869,8 @@ hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t 
   const int P = sp.P;
   const size_t sv = static_cast<size_t>(units) * DK * a.dv;  // one segment's S or N
   const size_t smm = static_cast<size_t>(units) * DK * DK;   // one segment's M
-  float* Sb = reinterpret_cast<float*>(
-      static_cast<unsigned char*>(a.ws) +
-      align256(static_cast<size_t>(units) * NC * ChunkBlock<OpT, DK, C>::kBytes));
+  const WsLayout wl = ws_layout(units, NC, ChunkBlock<OpT, DK, C>::kBytes, 1);
+  float* Sb = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + wl.seg);
   float* Nb = Sb + P * sv;
   float* Mb = Nb + P * sv;
   const int per_n = static_cast<int>(units) * (a.dv / 16);
@@ -1477,10 +1947,9 @@ size_t prefill_workspace_bytes(int B, int T, int H_v, int dk, int dv, int chunk,
   if (B <= 0 || T <= 0) return 0;
   const size_t nc = (static_cast<size_t>(T) + chunk - 1) / chunk;
   const size_t bb = io_bf16 ? block_bytes_rt<bf16>(dk, chunk) : block_bytes_rt<float>(dk, chunk);
-  const size_t blocks = static_cast<size_t>(B) * H_v * nc * bb;
   const SegPlan sp = carry_segments(B, T, H_v, dk, dv, chunk);
-  if (sp.P < 3) return blocks;
-  return align256(blocks) + seg_bytes(sp, static_cast<long>(B) * H_v, dk, dv);
+  const long units = static_cast<long>(B) * H_v;
+  return ws_layout(units, nc, bb, seg_bytes(sp, units, dk, dv)).total;
 }
 
 // Scratch of the allocation-free prefill entry point: the workspace of one

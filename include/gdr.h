@@ -61,8 +61,10 @@ typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  *   GDR_GATE_SCALAR_FUSED gate_in = x  [B,H_v]    / [B,T,H_v], with A_log and
  *                         dt_bias [H_v]: g = -exp(A_log[h]) * softplus(x + dt_bias[h])
  * All gate tensors are fp32.  A_log and dt_bias must be NULL for the other kinds
- * or are ignored.  Channel g must be <= 0; the chunked prefill additionally
- * requires chunk * max|g| <= 80 so that exp(+-prefix) stays finite in fp32. */
+ * or are ignored.  Channel and scalar g must be <= 0 (a decay, not a growth);
+ * any strength of decay is supported: the chunked prefill evaluates only
+ * exponentials of non-positive arguments (it forms the chunk's causal terms
+ * exactly once a chunk decays by more than e^-64 on some channel). */
 typedef enum gdr_gate {
   GDR_GATE_CHANNEL = 0,
   GDR_GATE_SCALAR = 1,

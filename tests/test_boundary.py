@@ -185,15 +185,36 @@ def test_noalloc_limit_is_the_workspace_of_the_t4000_workload():
     assert size(4032) <= gdr.binding.NOALLOC_SCRATCH_BYTES < size(4033)
 
 
+def _al(x, n):
+    return -(-x // n) * n
+
+
+def block_bytes(dk, chunk, es):
+    """One (b, h, chunk) block: Kt, Qt, Ke^T (chunk x dk each), Tb and P (chunk x
+    chunk each) in the operand type, then e^Gamma_L (dk fp32), 16-byte aligned."""
+    return _al((3 * chunk * dk + 2 * chunk * chunk) * es + 4 * dk, 16)
+
+
+def layout_bytes(units, nc, bb, seg=0):
+    """Chunk blocks; the segmented carry's buffers (if any) at the next 256-byte
+    boundary."""
+    end = units * nc * bb
+    return _al(end, 256) + seg if seg else end
+
+
 def test_workspace_size_query():
     lib = gdr.load_library()
-    size = lambda **kw: lib.gdr_prefill_workspace_size(ctypes.byref(_dims(**kw)), 1, 0)
+    size = lambda io=1, gate=0, **kw: lib.gdr_prefill_workspace_size(ctypes.byref(_dims(**kw)), io, gate)
     assert size(T=0) == 0 and size(B=0) == 0
     assert size(dk=48) == 0 and size(chunk=8) == 0
+    units = 2 * 4                                  # B=2, H_v=4 (the _dims defaults)
+    for io, es in ((1, 2), (0, 4)):
+        for T, C in ((1, 16), (16, 16), (17, 16), (100, 32), (129, 64)):
+            nc = -(-T // C)
+            expect = layout_bytes(units, nc, block_bytes(32, C, es))
+            for gate in (0, 1, 2):
+                assert size(io=io, gate=gate, T=T, chunk=C) == expect, (io, T, C, gate)
     assert size(T=16) == size(T=1) > 0            # one chunk either way
-    assert size(T=17) == 2 * size(T=16)
-    assert size(B=4) == 2 * size(B=2)
-    assert size(T=64, chunk=64) == lib.gdr_prefill_workspace_size(ctypes.byref(_dims(T=64, chunk=64)), 1, 2)
 
 
 def test_workspace_size_segmented_carry():
@@ -207,16 +228,17 @@ def test_workspace_size_segmented_carry():
         return lib.gdr_prefill_workspace_size(ctypes.byref(_dims(**kw)), 1, 0)
 
     kw = dict(B=1, H_qk=1, H_v=2, dk=128, dv=128, chunk=64)
-    block = size(T=64, **kw) // 2                  # one chunk block per unit
+    bb = block_bytes(128, 64, 2)
+    assert bb == 66048
     for T in (3000, 20000):
         P = carry_segments(1, T, 2, 128, 128, 64)
         assert P >= 3
-        blocks = 2 * (-(-T // 64)) * block
+        nc = -(-T // 64)
         extra = P * 2 * 128 * (2 * 128 + 128) * 4
-        assert size(T=T, **kw) == -(-blocks // 256) * 256 + extra
+        assert size(T=T, **kw) == layout_bytes(2, nc, bb, extra)
     # many units: one walk, chunk blocks only
     assert carry_segments(1, 3000, 32, 128, 128, 64) == 1
-    assert size(T=3000, B=1, H_qk=16, H_v=32, dk=128, dv=128, chunk=64) == 32 * 47 * block
+    assert size(T=3000, B=1, H_qk=16, H_v=32, dk=128, dv=128, chunk=64) == layout_bytes(32, 47, bb)
 
 
 def test_missing_library_raises(tmp_path):

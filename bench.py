@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the gated delta rule on one MI355X.
 
-Two legs, both on seeded synthetic inputs already resident in HBM:
+Three default legs, on seeded synthetic inputs already resident in HBM:
 
   decode   gdr_decode_step on the batched channelwise workload: B=64,
            H_qk=16 -> H_v=32, dk=dv=128, bf16 packed q|k|v rows, fp32 state
@@ -15,6 +15,9 @@ Two legs, both on seeded synthetic inputs already resident in HBM:
   prefill  gdr_prefill_chunked on B=1, T=4000, chunk 64, H 16 -> 32,
            dk=dv=128, bf16, channelwise gate, zero initial state.  Reported as
            tokens/s, with the fraction of the HBM and bf16 MFMA peaks.
+  long     gdr_prefill_chunked on B=4, T=32767, chunk 64, H 16 -> 32,
+           dk=dv=128, bf16, carried-in state, scalar and channelwise gates
+           (under "prefill_long"), reported like the prefill leg.
 
 Opt-in legs: sweep (T decode steps against one prefill), segmented (B=1,
 H 2 -> 4, T=32767: the long prefill over few heads that takes the segmented
@@ -23,7 +26,8 @@ carry, under "prefill_segmented") and copy (HBM-counter calibration).
 Prints one JSON line.  `value` is the decode GB/s; the prefill figures sit
 under "prefill".  Each leg carries its roofline (kernel time from HIP events
 recorded around every launch on the launch stream) and the fp64 CPU oracle
-timed on a bounded sample of the same workload ("cpu_baseline").
+timed on a bounded sample of the same workload ("cpu_baseline": all host
+cores, with a one-thread figure under "single_thread").
 """
 from __future__ import annotations
 
@@ -248,26 +252,37 @@ def inplace_ceiling(S, K):
                 kernel="torch in-place mul_ on the fp32 state (graph replay)")
 
 
-def cpu_decode(case, seconds):
+def _cpu_decode_mode(case, seconds, threads):
     import oracle
 
     t = case.tensors
-    thr = oracle.threads_used(cpu_threads())
+    thr = oracle.threads_used(threads)
     S = t["S0"].astype(np.float64)
     steps = 0
     t0 = time.perf_counter()
     while steps < t["qkv"].shape[0]:
-        oracle.decode(synth.bf16_to_f32(t["qkv"][steps]), case.H_qk, case.H_v, case.dk, case.dv,
-                      case.gate, t["gate_in"][steps], t["beta_logit"][steps], S, threads=thr)
+        _, S = oracle.decode(synth.bf16_to_f32(t["qkv"][steps]), case.H_qk, case.H_v, case.dk,
+                             case.dv, case.gate, t["gate_in"][steps], t["beta_logit"][steps], S,
+                             threads=thr)
         steps += 1
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
     nbytes = decode_bytes_per_step(case.B, case.H_qk, case.H_v, case.dk, case.dv)
     return dict(value=nbytes * steps / el / 1e9, unit="GB/s", cores=thr, kind="oracle",
-                host=host_cpu(),
                 sample=f"{steps} consecutive decode steps of the B={case.B} batch "
-                       f"({el:.1f} s, fp64 C recurrence, OpenMP over (b,h))")
+                       f"({el:.1f} s, fp64 C recurrence"
+                       + (", OpenMP over (b,h))" if thr > 1 else ", one thread)"))
+
+
+def cpu_decode(case, seconds):
+    """The fp64 oracle on the decode workload: all host cores (the reported
+    baseline) and one thread, each time-boxed."""
+    out = _cpu_decode_mode(case, seconds, cpu_threads())
+    out["host"] = host_cpu()
+    out["nproc"] = os.cpu_count()
+    out["single_thread"] = _cpu_decode_mode(case, seconds / 2, 1)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -346,6 +361,65 @@ def bench_prefill(reps, warm):
                                                    source_digest("prefill.hip"))),
         case=case,
     )
+
+
+def bench_prefill_long(gate, reps=3, warm=1, seed=None, cpu_seconds=0.0):
+    """The long prefill with a carried-in state: B=4, T=32767 (511 chunks of 64
+    and one of 63), H_qk=16 -> H_v=32, dk=dv=128, bf16 io, fp32 state with
+    S0 ~ N(0, 0.02^2); q, k, v ~ N(0,1) rounded to bf16, log-decay
+    g ~ -U(0.001, 0.2) per (b, t, h) (scalar gate) or per (b, t, h, channel)
+    (channel gate), beta logits ~ N(0,1).  Drawn on the device from a seeded
+    torch generator in that order (the 4 GB of inputs would take a minute to
+    draw on the host).  Graph replay of `reps` calls, as in the prefill leg."""
+    B, T, H_qk, H_v, dk, dv, C = 4, 32767, 16, 32, 128, 128, 64
+    channel = gate == synth.GATE_CHANNEL
+    if seed is None:
+        seed = 52 if channel else 51
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    bf = torch.bfloat16
+    q = torch.randn(B, T, H_qk, dk, device=DEV, generator=gen).to(bf)
+    k = torch.randn(B, T, H_qk, dk, device=DEV, generator=gen).to(bf)
+    v = torch.randn(B, T, H_v, dv, device=DEV, generator=gen).to(bf)
+    gshape = (B, T, H_v, dk) if channel else (B, T, H_v)
+    g = -(torch.rand(gshape, device=DEV, generator=gen) * 0.199 + 0.001)
+    bl = torch.randn(B, T, H_v, device=DEV, generator=gen)
+    S0 = torch.randn(B, H_v, dk, dv, device=DEV, generator=gen) * 0.02
+    S = torch.empty_like(S0)
+    o = torch.empty((B, T, H_v, dv), dtype=bf, device=DEV)
+    ws_bytes = gdr.gdr_prefill_workspace_size(B, T, H_qk, H_v, dk, dv, C, bf, gate)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    kw = dict(H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, chunk=C, gate=gate)
+
+    def run_all():
+        for _ in range(reps):
+            gdr.gdr_prefill_chunked(q, k, v, g, bl, S0, S, o, ws, **kw)
+
+    for _ in range(warm):
+        run_all()
+    sec = graph_us(run_all, reps=2) / reps / 1e6
+    flops = prefill_flops(T, B, H_v, dk, dv, C)
+    nbytes = prefill_bytes(T, B, H_qk, H_v, dk, dv, channel=channel, state_in=True)
+    out = dict(
+        value=B * T / sec, unit="tokens/s", ms_per_call=sec * 1e3,
+        timing=f"HIP events around graph replays of {reps} calls, / calls",
+        workload=f"long_prefill_{'channel' if channel else 'scalar'}: B={B}, T={T}, "
+                 f"H_qk={H_qk}->H_v={H_v}, dk=dv={dk}, chunk {C}, "
+                 f"{'channelwise' if channel else 'scalar'} gate, bf16 io, S0 ~ N(0, 0.02^2)",
+        workspace_bytes=ws_bytes,
+        roofline=dict(bound="hbm", achieved=nbytes / sec / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                      mfma_achieved_tflops=flops / sec / 1e12,
+                      mfma_peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+                      mfma_frac=flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      algorithmic_bytes=nbytes, algorithmic_flops=flops, traffic=None),
+    )
+    if cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_prefill(device_fetch(q, k, v, g, bl, S0, H_v // H_qk), B, T,
+                                          H_qk, H_v, gate, cpu_seconds)
+    del q, k, v, g, bl, S0, S, o, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_prefill_segmented(reps=4, warm=1):
@@ -477,36 +551,69 @@ def bench_sweep(batches=(1, 16), ts=SWEEP_TS, seed=11):
                 batches=out)
 
 
-def cpu_prefill(case, seconds):
+def _cpu_prefill_mode(fetch, B, T, H_qk, H_v, gate, seconds, threads):
+    """The oracle over whole sequences of (b, h) units, `thr` value heads of one
+    batch row at a time, until the time box is spent; tokens/s scaled to all
+    B * H_v units.  fetch(b, h0, h1) returns (q, k, v, gate_in, beta_logit,
+    S0) as host arrays for value heads h0 .. h1 - 1 of batch row b (q and k
+    for the query/key heads they use)."""
     import oracle
 
-    t = case.tensors
-    thr = oracle.threads_used(cpu_threads())
-    # Whole sequences of value heads (b=0), `thr` heads at a time, until time is up.
-    rep = case.H_v // case.H_qk
-    heads = 0
+    thr = oracle.threads_used(threads)
+    rep = H_v // H_qk
+    step = max(rep, thr - thr % rep)
+    units = 0
     t0 = time.perf_counter()
-    while heads < case.H_v:
-        hs = list(range(heads, min(case.H_v, heads + thr)))
-        hq = sorted({h // rep for h in hs})
-        # heads in hs use query/key heads hq; pass a sub-problem with those heads
-        sub_q = synth.bf16_to_f32(t["q"][:, :, hq[0]:hq[-1] + 1])
-        sub_k = synth.bf16_to_f32(t["k"][:, :, hq[0]:hq[-1] + 1])
-        lo = hq[0] * rep
-        hi = (hq[-1] + 1) * rep
-        oracle.sequence(sub_q, sub_k, synth.bf16_to_f32(t["v"][:, :, lo:hi]), case.gate,
-                        t["gate_in"][:, :, lo:hi], t["beta_logit"][:, :, lo:hi],
-                        t["S0"][:, lo:hi], threads=thr)
-        heads = hi
+    for b in range(B):
+        for h0 in range(0, H_v, step):
+            h1 = min(H_v, h0 + step)
+            q, k, v, g, bl, s0 = fetch(b, h0, h1)
+            oracle.sequence(q, k, v, gate, g, bl, s0, threads=thr)
+            units += h1 - h0
+            if time.perf_counter() - t0 >= seconds:
+                break
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
-    frac = heads / case.H_v
-    return dict(value=case.B * case.T * frac / el, unit="tokens/s", cores=thr, kind="oracle",
-                host=host_cpu(),
-                sample=f"{heads} of {case.H_v} value heads over all {case.T} tokens "
-                       f"({el:.1f} s, fp64 token recurrence, OpenMP over heads); "
-                       f"tokens/s scaled to all heads")
+    frac = units / (B * H_v)
+    return dict(value=B * T * frac / el, unit="tokens/s", cores=thr, kind="oracle",
+                sample=f"{units} of {B * H_v} (b, h) units over all {T} tokens ({el:.1f} s, "
+                       f"fp64 token recurrence"
+                       + (", OpenMP over heads" if thr > 1 else ", one thread")
+                       + "); tokens/s scaled to all units")
+
+
+def cpu_prefill(fetch, B, T, H_qk, H_v, gate, seconds):
+    """All host cores (the reported baseline) and one thread, each time-boxed."""
+    out = _cpu_prefill_mode(fetch, B, T, H_qk, H_v, gate, seconds, cpu_threads())
+    out["host"] = host_cpu()
+    out["nproc"] = os.cpu_count()
+    out["single_thread"] = _cpu_prefill_mode(fetch, B, T, H_qk, H_v, gate, seconds / 2, 1)
+    return out
+
+
+def host_fetch(case):
+    """fetch() for cpu_prefill from a host-side case (bf16 expanded exactly)."""
+    t = case.tensors
+    rep = case.H_v // case.H_qk
+
+    def fetch(b, h0, h1):
+        sl = slice(b, b + 1)
+        f = synth.bf16_to_f32
+        return (f(t["q"][sl, :, h0 // rep:(h1 - 1) // rep + 1]),
+                f(t["k"][sl, :, h0 // rep:(h1 - 1) // rep + 1]), f(t["v"][sl, :, h0:h1]),
+                t["gate_in"][sl, :, h0:h1], t["beta_logit"][sl, :, h0:h1], t["S0"][sl, h0:h1])
+    return fetch
+
+
+def device_fetch(q, k, v, g, bl, s0, rep):
+    """fetch() for cpu_prefill from device tensors (copied to the host)."""
+    def fetch(b, h0, h1):
+        c = lambda x: x.float().cpu().numpy()
+        return (c(q[b:b + 1, :, h0 // rep:(h1 - 1) // rep + 1]),
+                c(k[b:b + 1, :, h0 // rep:(h1 - 1) // rep + 1]), c(v[b:b + 1, :, h0:h1]),
+                c(g[b:b + 1, :, h0:h1]), c(bl[b:b + 1, :, h0:h1]), c(s0[b:b + 1, h0:h1]))
+    return fetch
 
 
 def copy_calibration(reps=8, nbytes=256 << 20):
@@ -528,9 +635,10 @@ def main():
     ap.add_argument("--batch", type=int, default=64, help="decode batch (64 is the workload)")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=3)
-    ap.add_argument("--legs", default="decode,prefill",
-                    help="comma list of decode, prefill, sweep (T-sweep of decode steps against "
-                         "one prefill), segmented (a long prefill over few heads: the "
+    ap.add_argument("--legs", default="decode,prefill,long",
+                    help="comma list of decode, prefill, long (B=4, T=32767 with a carried-in "
+                         "state, scalar and channel gates), sweep (T-sweep of decode steps "
+                         "against one prefill), segmented (a long prefill over few heads: the "
                          "segmented carry), copy (HBM-counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time box of each CPU-oracle baseline (0 disables)")
@@ -559,6 +667,14 @@ def main():
         pre = bench_prefill(args.prefill_reps, args.prefill_warmup)
         print(f"[bench] prefill done: {pre['value']:.3e} tok/s", file=sys.stderr, flush=True)
 
+    long_legs = None
+    if "long" in legs:
+        long_legs = {}
+        for name, gate in (("scalar", synth.GATE_SCALAR), ("channel", synth.GATE_CHANNEL)):
+            long_legs[name] = bench_prefill_long(gate, cpu_seconds=args.cpu_seconds)
+            print(f"[bench] long prefill ({name} gate) done: "
+                  f"{long_legs[name]['value']:.3e} tok/s", file=sys.stderr, flush=True)
+
     sweep = None
     if "sweep" in legs:
         sweep = bench_sweep()
@@ -579,7 +695,9 @@ def main():
         if dec is not None:
             cpu_dec = cpu_decode(dec["case"], args.cpu_seconds)
         if pre is not None:
-            cpu_pre = cpu_prefill(pre["case"], args.cpu_seconds)
+            c = pre["case"]
+            cpu_pre = cpu_prefill(host_fetch(c), c.B, c.T, c.H_qk, c.H_v, c.gate,
+                                  args.cpu_seconds)
         print("[bench] cpu baselines done", file=sys.stderr, flush=True)
 
     if dec is not None:
@@ -610,6 +728,8 @@ def main():
                         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                         "data": "synthetic", "config": {"workload": pre["workload"]},
                         "roofline": pre["roofline"], "cpu_baseline": cpu_pre})
+    if long_legs is not None:
+        out["prefill_long"] = long_legs
     if sweep is not None:
         out["sweep"] = sweep
     if seg is not None:

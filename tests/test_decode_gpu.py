@@ -103,13 +103,13 @@ def test_decode_fused_gate_bf16_b1():
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_decode_batched_channel_b64_256_steps():
-    """B=64 channelwise decode, 256 consecutive steps, all of them on the GPU;
-    the oracle follows six sampled batch rows through every step."""
+    """B=64 channelwise decode, 256 consecutive steps: every output of every
+    step and the final state of all 64 batch rows against the oracle."""
     case = synth.batched_decode(seed=3, steps=256, B=64)
-    announce("decode batched channel bf16 B=64 H 16->32 dk=dv=128 steps=256")
-    eo, es = _decode_run(case, 256, rows=[0, 5, 17, 32, 50, 63])
+    announce("decode batched channel bf16 B=64 H 16->32 dk=dv=128 steps=256 (all rows)")
+    eo, es = _decode_run(case, 256)
     print(f"err o={eo:.3e} S={es:.3e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 

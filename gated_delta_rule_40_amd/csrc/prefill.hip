@@ -1182,7 +1182,7 @@ struct CarryFrags {
   typename Sh::FK::T kt[Sh::OPW][Sh::FK::STEPS], qt[Sh::OPW][Sh::FK::STEPS];
   typename Sh::FC::T tb[Sh::OPW][Sh::FC::STEPS], p[Sh::OPW][Sh::FC::STEPS];
   typename Sh::FC::T ke[Sh::SPW][Sh::FC::STEPS];
-  float v[Sh::OPW][4];
+  OpT v[Sh::OPW][4];  // as loaded (widened to fp32 where used, so the load is not waited for early)
   float gam[Sh::SPW][4];
 };
 
@@ -1220,11 +1220,11 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = min(16 * R + 4 * (lane >> 4) + e, last);
-            F.v[i][e] = to_f32(vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)]);
+            F.v[i][e] = vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)];
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) F.v[i][e] = 0.0f;
+          for (int e = 0; e < 4; ++e) F.v[i][e] = from_f32<OpT>(0.0f);
         }
       }
       if constexpr (PHASE == 1) {
@@ -1274,7 +1274,7 @@ __device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C>& F, con
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = min(16 * R + 4 * (lane >> 4) + e, last);
-    F.v[i][e] = to_f32(vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)]);
+    F.v[i][e] = vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)];
   }
 }
 
@@ -1376,6 +1376,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
   // memory operations, which keeps the compiler's wait counts exact.
   auto compute = [&](Frags& F, int nn, auto full) __attribute__((always_inline)) {
     constexpr bool kFull = decltype(full)::value;
+    constexpr bool kPin = Sh::kPinLoads;
     const int t0 = nn * C;
     const int L = kFull ? C : min(C, a.T - t0);
     const int nx = min(nn + 1, cr.n1 - 1);
@@ -1412,15 +1413,16 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
           if constexpr (MODE == kCarryFull) oacc[i] = FK::mma(z[s], F.qt[i][s], oacc[i]);
           // The next chunk's fragments go out one pair per step, each as soon
           // as its registers have been read.
+          pin_order<kPin>();  // the reloads below may then reuse the consumed registers
           F.kt[i][s] = FK::load(nblk + Blk::kKt, 16 * R, s, lane);
           if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
-          pin_order<Sh::kPinLoads>();
+          pin_order<kPin>();
         }
         float rv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * R + 4 * (lane >> 4) + e;
-          rv[e] = (r < L ? F.v[i][e] : 0.0f) - ks[e];
+          rv[e] = (r < L ? to_f32(F.v[i][e]) : 0.0f) - ks[e];
         }
         store_tile_t<OpT>(Rt_s, LDC, 16 * J, 16 * R, rv, lane);
         if constexpr (MODE != kCarryMapM) carry_load_v<OpT, DK, DVS, C>(F, a, nx, b, h, jb, i, R, J, lane);
@@ -1438,8 +1440,9 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s) {
           u = FC::mma(F.tb[i][s], FC::load_pad(Rt_s, LDC, 16 * J, s, lane), u);
+          pin_order<kPin>();
           F.tb[i][s] = FC::load(nblk + Blk::kTb, 16 * R, s, lane);
-          pin_order<Sh::kPinLoads>();
+          pin_order<kPin>();
         }
         float uv[4] = {u[0], u[1], u[2], u[3]};
         store_tile_t<OpT>(Ut_s, LDC, 16 * J, 16 * R, uv, lane);
@@ -1467,8 +1470,9 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
             pacc[i] = FC::mma(FC::load_pad(Ut_s, LDC, 16 * J, s, lane), F.p[i][s], pacc[i]);
           else
             oacc[i] = FC::mma(FC::load_pad(Ut_s, LDC, 16 * J, s, lane), F.p[i][s], oacc[i]);
+          pin_order<kPin>();
           F.p[i][s] = FC::load(nblk + Blk::kP, 16 * R, s, lane);
-          pin_order<Sh::kPinLoads>();
+          pin_order<kPin>();
         }
       }
     }
@@ -1483,8 +1487,9 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
 #pragma unroll
         for (int s = 0; s < FC::STEPS; ++s) {
           t = FC::mma(F.ke[i][s], FC::load_pad(Ut_s, LDC, 16 * J, s, lane), t);
+          pin_order<kPin>();
           F.ke[i][s] = FC::load(nblk + Blk::kKeT, 16 * I, s, lane);
-          pin_order<Sh::kPinLoads>();
+          pin_order<kPin>();
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[i][e] = F.gam[i][e] * sacc[i][e] + t[e];
@@ -1526,7 +1531,12 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
   carry_load_all<OpT, DK, DVS, C, MODE>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
   const int NF = a.T / C;  // full chunks
   const int nf_end = min(cr.n1, NF);
-  for (int nn = cr.n0; nn < nf_end; ++nn) compute(F, nn, std::true_type{});
+  int nn = cr.n0;
+  for (; nn + 1 < nf_end; nn += 2) {
+    compute(F, nn, std::true_type{});
+    compute(F, nn + 1, std::true_type{});
+  }
+  if (nn < nf_end) compute(F, nn, std::true_type{});
   if (cr.n1 > NF) compute(F, NF, std::false_type{});  // the ragged last chunk
 
   // ---- final state ----

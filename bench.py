@@ -412,7 +412,10 @@ def bench_prefill_long(gate, reps=3, warm=1, seed=None, cpu_seconds=0.0):
                       mfma_achieved_tflops=flops / sec / 1e12,
                       mfma_peak_tflops=MFMA_BF16_PEAK_TFLOPS,
                       mfma_frac=flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                      algorithmic_bytes=nbytes, algorithmic_flops=flops, traffic=None),
+                      algorithmic_bytes=nbytes, algorithmic_flops=flops,
+                      traffic=traffic_from_profile(
+                          f"long_prefill_{'channel' if channel else 'scalar'}",
+                          source_digest("prefill.hip"))),
     )
     if cpu_seconds > 0:
         out["cpu_baseline"] = cpu_prefill(device_fetch(q, k, v, g, bl, S0, H_v // H_qk), B, T,

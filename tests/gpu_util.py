@@ -101,24 +101,21 @@ def run_prefill(case: synth.Case, chunk=None, state_in="S0", scale=1.0, l2norm=T
 
 
 def carry_segments(B, T, H_v, dk, dv, chunk):
-    """The library's choice of carry segments for a chunked prefill (1: one
-    walk over the sequence), mirrored from its host routing so that tests know
-    which cases take the segmented carry."""
-    NC = -(-T // chunk)
-    units = B * H_v
-    w_n, w_m = units * (dv // 16), units * (dk // 16)
-    if w_n > 128:
+    """How many sequence segments the library's carry uses for a chunked
+    prefill (1: one walk over the sequence), read from its own workspace
+    query: the segmented carry appends P x units x dk x (2 dv + dk) fp32 words
+    (segment states, maps N and M) after the chunk blocks, at the next 256-byte
+    boundary.  Nothing of the library's planning rule is restated here."""
+    def size(b, t, h):
+        return gdr.gdr_prefill_workspace_size(b, t, 1, h, dk, dv, chunk, torch.bfloat16, 0)
+
+    block = size(1, 1, 1)                     # one unit, one chunk: one block, no segments
+    units, nc = B * H_v, -(-T // chunk)
+    blocks = units * nc * block
+    total = size(B, T, H_v)
+    if total == blocks:
         return 1
-    max_wgs = 1024 if NC >= 256 else 512
-    best = 1
-    for P in range(3, 17):
-        L = -(-NC // P)
-        if L < 8:
-            break
-        Pe = -(-NC // L)
-        if Pe < 3:
-            continue
-        if w_n + (Pe - 2) * (w_n + w_m) > max_wgs:
-            break
-        best = Pe
-    return best
+    per_seg = units * dk * (2 * dv + dk) * 4
+    extra = total - (-(-blocks // 256) * 256)
+    assert extra > 0 and extra % per_seg == 0, (total, blocks, per_seg)
+    return extra // per_seg

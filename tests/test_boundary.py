@@ -220,8 +220,9 @@ def test_workspace_size_query():
 def test_workspace_size_segmented_carry():
     """Long prefills over few units take the segmented carry: the size query
     adds its fp32 segment states and maps (S and N: P x units x dk x dv, M:
-    P x units x dk x dk) after the chunk blocks, aligned to 256 bytes."""
-    from tests.gpu_util import carry_segments
+    P x units x dk x dk) after the chunk blocks, aligned to 256 bytes, for P
+    from 3 to 16 segments of at least 8 chunks each; many units keep one walk
+    and the chunk blocks alone."""
     lib = gdr.load_library()
 
     def size(**kw):
@@ -230,15 +231,19 @@ def test_workspace_size_segmented_carry():
     kw = dict(B=1, H_qk=1, H_v=2, dk=128, dv=128, chunk=64)
     bb = block_bytes(128, 64, 2)
     assert bb == 66048
+    per_seg = 2 * 128 * (2 * 128 + 128) * 4
     for T in (3000, 20000):
-        P = carry_segments(1, T, 2, 128, 128, 64)
-        assert P >= 3
         nc = -(-T // 64)
-        extra = P * 2 * 128 * (2 * 128 + 128) * 4
-        assert size(T=T, **kw) == layout_bytes(2, nc, bb, extra)
+        extra = size(T=T, **kw) - layout_bytes(2, nc, bb, 1) + 1
+        assert extra > 0 and extra % per_seg == 0, (T, extra)
+        P = extra // per_seg
+        assert 3 <= P <= 16 and -(-nc // P) >= 8, (T, P)
     # many units: one walk, chunk blocks only
-    assert carry_segments(1, 3000, 32, 128, 128, 64) == 1
     assert size(T=3000, B=1, H_qk=16, H_v=32, dk=128, dv=128, chunk=64) == layout_bytes(32, 47, bb)
+    # the GPU tests' reading of the plan agrees with the same query
+    from tests.gpu_util import carry_segments
+    assert carry_segments(1, 3000, 32, 128, 128, 64) == 1
+    assert carry_segments(1, 20000, 2, 128, 128, 64) >= 3
 
 
 def test_missing_library_raises(tmp_path):

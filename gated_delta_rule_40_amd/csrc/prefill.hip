@@ -1144,7 +1144,12 @@ struct CarryShape {
   static constexpr int P = pad_of<OpT>();
   static constexpr int LDK = DK + P;  // rows of St
   static constexpr int LDC = C + P;   // rows of Rt, Ut
-  static constexpr int NW = DVS >= 32 ? 8 : 4;        // waves (two per SIMD from 32 columns)
+  // Four waves, one per SIMD, at every width: the output tiles of one row
+  // block go to one wave, so each fragment of Kt, Qt, Tb and P is loaded once
+  // per workgroup.  With eight waves two of them shared each row block and
+  // loaded its fragments twice (B=2, T=4000: 262 -> 242 us per prefill; B=4,
+  // T=32767: 2.90 -> 2.82 ms).
+  static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int DVT = DVS / 16;
   static constexpr int NST = (DK / 16) * DVT;         // state tiles
@@ -1153,10 +1158,10 @@ struct CarryShape {
   static constexpr int OPW = (NOT + NW - 1) / NW;
   static constexpr size_t kSmem = sizeof(OpT) * (DVS * LDK + 2 * DVS * LDC);
   // Keep each next-chunk load where it is written (right after the MFMA that
-  // last reads its registers) when a wave owns one output tile; with two the
+  // last reads its registers) when a wave owns one output tile; with more the
   // pinned order costs more registers than it saves (64-column slices:
-  // 3.8 ms against 3.4 ms at B=4, T=32767; 16 columns: 148 us against 166 us
-  // unpinned at B=1, T=4000).
+  // 3.8 ms against 3.4 ms at B=4, T=32767, measured with eight waves;
+  // 16 columns: 148 us against 166 us unpinned at B=1, T=4000).
   static constexpr bool kPinLoads = OPW == 1;
   // With 16-column slices each o store is a 16 C-byte piece (32 bytes in
   // bf16) of a row that the 8 slices of the head share; written with the
@@ -1188,6 +1193,12 @@ struct CarryFrags {
 
 // Issue the loads of chunk nn's fragments for this wave's tiles, by phase:
 // phase c needs Kt, Qt and V; phase d Tb; phase e P, Ke^T and e^Gamma_L.
+// Where the loop pins its reloads (kPinLoads), each load here is fenced in
+// place too, so that these first loads go out in the order the chunk loop
+// issues its reloads: the compiler's wait counts at the top of the loop take
+// the worse of the entry path and the loop's own, and a reordered entry (a Qt
+// fragment requested among the last) made every loop trip wait for nearly all
+// of the previous step's loads.
 template <typename OpT, int DK, int DVS, int C, int PHASE, int MODE>
 __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
                                            const unsigned char* ws_head, int nn, int b, int h,
@@ -1209,7 +1220,9 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
 #pragma unroll
         for (int s = 0; s < FK::STEPS; ++s) {
           F.kt[i][s] = FK::load(blk + Blk::kKt, 16 * R, s, lane);
+          pin_order<Sh::kPinLoads>();
           if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(blk + Blk::kQt, 16 * R, s, lane);
+          pin_order<Sh::kPinLoads>();
         }
         if constexpr (MODE != kCarryMapM) {
           // Uniform row base plus 32-bit lane offsets; rows past the end
@@ -1222,6 +1235,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
             const int r = min(16 * R + 4 * (lane >> 4) + e, last);
             F.v[i][e] = vrow[static_cast<unsigned>(r) * rs + 16 * J + (lane & 15)];
           }
+          pin_order<Sh::kPinLoads>();
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) F.v[i][e] = from_f32<OpT>(0.0f);
@@ -1229,13 +1243,17 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
       }
       if constexpr (PHASE == 1) {
 #pragma unroll
-        for (int s = 0; s < FC::STEPS; ++s)
+        for (int s = 0; s < FC::STEPS; ++s) {
           F.tb[i][s] = FC::load(blk + Blk::kTb, 16 * R, s, lane);
+          pin_order<Sh::kPinLoads>();
+        }
       }
       if constexpr (PHASE == 2 && MODE == kCarryFull) {
 #pragma unroll
-        for (int s = 0; s < FC::STEPS; ++s)
+        for (int s = 0; s < FC::STEPS; ++s) {
           F.p[i][s] = FC::load(blk + Blk::kP, 16 * R, s, lane);
+          pin_order<Sh::kPinLoads>();
+        }
       }
     }
   }
@@ -1247,8 +1265,10 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
       if (Sh::NST % Sh::NW == 0 || t < Sh::NST) {
         const int I = t / Sh::DVT;
 #pragma unroll
-        for (int s = 0; s < FC::STEPS; ++s)
+        for (int s = 0; s < FC::STEPS; ++s) {
           F.ke[j][s] = FC::load(blk + Blk::kKeT, 16 * I, s, lane);
+          pin_order<Sh::kPinLoads>();
+        }
         const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
         F.gam[j][0] = g4.x;
         F.gam[j][1] = g4.y;

@@ -99,7 +99,8 @@ int check_prefill(const PrefillCall& c, bool own_scratch, const void* workspace,
     if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.o, 16) ||
         !aligned(c.beta_logit, 4))
       return GDR_E_ALIGN;
-    *need = gdr::prefill_workspace_bytes(d.B, d.T, d.H_v, d.dk, d.dv, d.chunk, c.io == GDR_BF16);
+    *need = gdr::prefill_workspace_bytes(d.B, d.T, d.H_qk, d.H_v, d.dk, d.dv, d.chunk,
+                                         c.io == GDR_BF16, c.gate);
     if (!own_scratch) {
       if (!workspace || workspace_bytes < *need) return GDR_E_WORKSPACE;
       if (!aligned(workspace, 16)) return GDR_E_ALIGN;
@@ -153,6 +154,7 @@ int launch(const PrefillCall& c, void* workspace, hipStream_t stream) {
   a.state_out = c.state_out;
   a.o = c.o;
   a.ws = workspace;
+  a.ws_qk = nullptr;  // placed inside the workspace by the chunked launch
   a.B = d.B;
   a.T = d.T;
   a.H_qk = d.H_qk;
@@ -238,8 +240,8 @@ int gdr_decode_step(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const voi
 
 size_t gdr_prefill_workspace_size(const gdr_dims* dims, gdr_dtype io, gdr_gate gate) {
   if (check_sizes(dims, io, gate, true) != GDR_OK) return 0;
-  return gdr::prefill_workspace_bytes(dims->B, dims->T, dims->H_v, dims->dk, dims->dv,
-                                      dims->chunk, io == GDR_BF16);
+  return gdr::prefill_workspace_bytes(dims->B, dims->T, dims->H_qk, dims->H_v, dims->dk,
+                                      dims->dv, dims->chunk, io == GDR_BF16, gate);
 }
 
 int gdr_prefill_chunked(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const void* q,

@@ -42,13 +42,19 @@ struct PrefillArgs {
   float* state_out;         // [B,H_v,dk,dv]
   void* o;                  // [B,T,H_v,dv]
   void* ws;                 // workspace
+  void* ws_qk;              // scalar gates: the normalised k and q rows per (b, qk head, chunk),
+                            // inside the workspace (set by the chunked launch)
   int B, T, H_qk, H_v, dk, dv, chunk;
   int gate;
   int l2norm;
   float scale;
 };
 
-size_t prefill_workspace_bytes(int B, int T, int H_v, int dk, int dv, int chunk, int io_bf16);
+// Workspace bytes of a chunked prefill; scalar gates (any gate but
+// GDR_GATE_CHANNEL) take smaller chunk blocks plus the normalised k and q rows
+// once per qk head.
+size_t prefill_workspace_bytes(int B, int T, int H_qk, int H_v, int dk, int dv, int chunk,
+                               int io_bf16, int gate);
 hipError_t launch_prefill(const PrefillArgs& a, int io_bf16, hipStream_t stream);
 
 // The allocation-free prefill takes its workspace from a device array of this

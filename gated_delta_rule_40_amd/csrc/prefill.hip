@@ -168,16 +168,34 @@ struct FragT {
 // Layout of one (b, h, chunk) block of the workspace.  The operand regions are
 // in fragment order (FragT::slot_row / slot_col): Kt and Qt for a
 // contraction over DK, the others over C.
-template <typename OpT, int DK, int C>
+//
+// kRaw (scalar gates): with one decay per row, Kt = diag(e^Gamma) K and
+// Qt = diag(e^Gamma) Q are row scalings of the normalised k and q rows, which
+// do not depend on the value head.  The block of a value head then leaves Kt
+// and Qt out and holds the row factor e^Gamma_r instead (0 on the rows past
+// the end of a ragged last chunk); the normalised rows are stored once per
+// (b, qk head, chunk) in a QKRegion, and the carry scales its products row by
+// row.  With two value heads per qk head that is a quarter fewer bytes.
+template <typename OpT, int DK, int C, bool kRaw>
 struct ChunkBlock {
-  static constexpr int kKt = 0;                  // [C][DK]  K e^Gamma
-  static constexpr int kQt = C * DK;             // [C][DK]  Q e^Gamma
-  static constexpr int kKeT = 2 * C * DK;        // [DK][C]  (K e^(Gamma_L - Gamma))^T
-  static constexpr int kTb = 3 * C * DK;         // [C][C]   (I + A)^-1 diag(beta)
-  static constexpr int kP = 3 * C * DK + C * C;  // [C][C]   lower(Q K^T o D)
-  static constexpr int kOpElems = 3 * C * DK + 2 * C * C;
+  static constexpr int kKt = 0;                          // [C][DK]  K e^Gamma (not kRaw)
+  static constexpr int kQt = C * DK;                     // [C][DK]  Q e^Gamma (not kRaw)
+  static constexpr int kKeT = kRaw ? 0 : 2 * C * DK;     // [DK][C]  (K e^(Gamma_L - Gamma))^T
+  static constexpr int kTb = kKeT + C * DK;              // [C][C]   (I + A)^-1 diag(beta)
+  static constexpr int kP = kTb + C * C;                 // [C][C]   lower(Q K^T o D)
+  static constexpr int kOpElems = kP + C * C;
   static constexpr size_t kGammaByte = static_cast<size_t>(kOpElems) * sizeof(OpT);  // [DK] f32
-  static constexpr size_t kBytes = (kGammaByte + DK * sizeof(float) + 15) / 16 * 16;
+  static constexpr size_t kFacByte = kGammaByte + DK * sizeof(float);  // kRaw: e^Gamma [C] f32
+  static constexpr size_t kBytes = (kFacByte + (kRaw ? C * sizeof(float) : 0) + 15) / 16 * 16;
+};
+
+// Scalar gates: the normalised k rows and q rows of one (b, qk head, chunk),
+// each [C][DK] in fragment order (contraction over DK).
+template <typename OpT, int DK, int C>
+struct QKRegion {
+  static constexpr int kK = 0;
+  static constexpr int kQ = C * DK;
+  static constexpr size_t kBytes = 2 * static_cast<size_t>(C) * DK * sizeof(OpT);
 };
 
 // ---------------------------------------------------------------------------
@@ -346,7 +364,7 @@ __device__ __forceinline__ void emit_carry_operands(
     const typename PrepSmem<OpT, DK, C>::RowsOp& qtr, int rlo, bool active, int c4, OpT* out,
     unsigned char* sm, int tid) {
   using Sm = PrepSmem<OpT, DK, C>;
-  using Blk = ChunkBlock<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C, false>;
   OpT* r0 = reinterpret_cast<OpT*>(sm + Sm::oR0);
   OpT* r1 = reinterpret_cast<OpT*>(sm + Sm::oR1);
   if (active) {
@@ -374,14 +392,17 @@ __device__ __forceinline__ void lower_tile(int job, int& R, int& S) {
 // Causal terms for a scalar gate (one decay per row): the decays leave the
 // contraction, so A and P come from the plain products K K^T and Q K^T on
 // MFMA, each entry scaled by e^(Gamma_r - Gamma_s) <= 1 -- exact for any
-// decay.  Kt, Ke and Qt are per-row scalings with exponents <= 0.
+// decay.  Ke is a per-row scaling with exponents <= 0; Kt and Qt are not
+// stored: the block gets the row factor e^Gamma_r, and qk_out (the QKRegion of
+// this chunk's qk head, written by the first of its value heads; null for the
+// others) the normalised k and q rows.
 template <typename OpT, int DK, int C>
 __device__ __forceinline__ void prep_causal_scalar(
     const typename PrepSmem<OpT, DK, C>::RowsF& kq, const typename PrepSmem<OpT, DK, C>::RowsF& qq,
-    const typename PrepSmem<OpT, DK, C>::RowsF& gq, float gam0, float total, int rlo, bool active,
-    int c4, OpT* out, unsigned char* sm, int tid, int lane, int wave) {
+    const typename PrepSmem<OpT, DK, C>::RowsF& gq, float gam0, float total, int L, int rlo,
+    bool active, int c4, OpT* out, OpT* qk_out, unsigned char* sm, int tid, int lane, int wave) {
   using Sm = PrepSmem<OpT, DK, C>;
-  using Blk = ChunkBlock<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C, true>;
   constexpr int LDK = Sm::LDK, LDT = Sm::LDT, NB = Sm::NB, RPP = Sm::RPP;
   OpT* Kr_s = reinterpret_cast<OpT*>(sm + Sm::oR0);  // K rows as given
   OpT* Qr_s = reinterpret_cast<OpT*>(sm + Sm::oR1);  // Q rows as given
@@ -389,23 +410,20 @@ __device__ __forceinline__ void prep_causal_scalar(
   float* gam_s = reinterpret_cast<float*>(sm + Sm::oGam);
   const float* beta_s = reinterpret_cast<const float*>(sm + Sm::oBeta);
 
-  OpT ktr[RPP][4], ker[RPP][4], qtr[RPP][4];
+  OpT ker[RPP][4];
   if (active) {
     float gam = gam0;
 #pragma unroll
     for (int i = 0; i < RPP; ++i) {
       const int r = rlo + i;
       gam += gq[i][0];
-      const float ep = __builtin_amdgcn_exp2f(gam * kLog2e);
       const float ef = __builtin_amdgcn_exp2f((total - gam) * kLog2e);
       OpT kr[4], qr[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         kr[u] = from_f32<OpT>(kq[i][u]);
         qr[u] = from_f32<OpT>(qq[i][u]);
-        ktr[i][u] = from_f32<OpT>(kq[i][u] * ep);
         ker[i][u] = from_f32<OpT>(kq[i][u] * ef);
-        qtr[i][u] = from_f32<OpT>(qq[i][u] * ep);
       }
       store_vec4<OpT>(Kr_s + r * LDK + 4 * c4, kr);
       store_vec4<OpT>(Qr_s + r * LDK + 4 * c4, qr);
@@ -413,6 +431,14 @@ __device__ __forceinline__ void prep_causal_scalar(
     }
   }
   __syncthreads();
+  if (tid < C) {
+    float* fac = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(out) + Blk::kFacByte);
+    fac[tid] = tid < L ? __builtin_amdgcn_exp2f(gam_s[tid] * kLog2e) : 0.0f;
+  }
+  if (qk_out) {
+    lds_to_frag<OpT, DK, C>(qk_out + QKRegion<OpT, DK, C>::kK, Kr_s, LDK, tid);
+    lds_to_frag<OpT, DK, C>(qk_out + QKRegion<OpT, DK, C>::kQ, Qr_s, LDK, tid);
+  }
 
   // Lower tiles: A and P of a tile by one wave, computed transposed (each
   // lane holds four consecutive columns of one row) with one shared decay
@@ -448,8 +474,11 @@ __device__ __forceinline__ void prep_causal_scalar(
       frag_store<OpT, C, 4>(out + Blk::kP, 16 * R + (lane & 15), 16 * S + 4 * (lane >> 4), z);
     }
   }
-  __syncthreads();  // K and Q rows are dead
-  emit_carry_operands<OpT, DK, C>(ktr, ker, qtr, rlo, active, c4, out, sm, tid);
+  __syncthreads();  // K and Q rows are dead: Ke^T through R1, transposed
+  if (active) rows_to_lds<OpT, RPP>(Qr_s, LDK, rlo, c4, ker);
+  __syncthreads();
+  lds_to_frag_t<OpT, C, DK>(out + Blk::kKeT, Qr_s, LDK, tid);
+  __syncthreads();
 }
 
 // Causal terms for a channel gate whose chunk decays by at most
@@ -468,7 +497,7 @@ __device__ __forceinline__ bool prep_causal_factored(
     const float (&total)[4], bool strong, int rlo, bool active, int c4, OpT* out,
     unsigned char* sm, int tid, int lane, int wave) {
   using Sm = PrepSmem<OpT, DK, C>;
-  using Blk = ChunkBlock<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C, false>;
   constexpr int LDK = Sm::LDK, LDT = Sm::LDT, NB = Sm::NB, RPP = Sm::RPP;
   OpT* Kt_s = reinterpret_cast<OpT*>(sm + Sm::oR0);
   OpT* Qt_s = Kt_s;  // once A is done
@@ -649,7 +678,7 @@ __device__ __forceinline__ void prep_causal_exact(const PrefillArgs& a, size_t q
                                                   int c4, OpT* out, unsigned char* sm, int tid,
                                                   int lane, int wave) {
   using Sm = PrepSmem<OpT, DK, C>;
-  using Blk = ChunkBlock<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C, false>;
   using X = ExactPass<OpT, DK, C>;
   using F = FragT<OpT, X::KP>;
   constexpr int LDT = Sm::LDT, RPP = Sm::RPP, KP = X::KP, LDP = X::LDP;
@@ -830,7 +859,7 @@ template <typename OpT, int DK, int C, bool kChannel>
 __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, int wg, int G,
                                           unsigned char* sm) {
   using Sm = PrepSmem<OpT, DK, C>;
-  using Blk = ChunkBlock<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C, !kChannel>;
   constexpr int LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
   constexpr int PARTS = Sm::PARTS, RPP = Sm::RPP;
 
@@ -927,7 +956,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
   //         one thread per row adds them up ----
   float* nrm = reinterpret_cast<float*>(sm + Sm::oR0);  // [C][2 NQ + 1] partials, then 1/norms
   float* nrm_s = reinterpret_cast<float*>(sm + Sm::oNrm);
-  if (kChannel && !a.l2norm && tid < C) {
+  if (!a.l2norm && tid < C) {
     nrm_s[2 * tid] = 1.0f;
     nrm_s[2 * tid + 1] = 1.0f;
   }
@@ -954,10 +983,10 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
       }
       nrm[tid * Sm::LDN] = 1.0f / sqrtf(sk + kL2Eps);
       nrm[tid * Sm::LDN + 1] = 1.0f / sqrtf(sq + kL2Eps);
-      if constexpr (kChannel) {  // kept for the exact routine, which reads k and q again
-        nrm_s[2 * tid] = nrm[tid * Sm::LDN];
-        nrm_s[2 * tid + 1] = nrm[tid * Sm::LDN + 1];
-      }
+      // kept for the exact routine, which reads k and q again, and for the
+      // scalar gate's row factors
+      nrm_s[2 * tid] = nrm[tid * Sm::LDN];
+      nrm_s[2 * tid + 1] = nrm[tid * Sm::LDN + 1];
     }
     __syncthreads();
     if (active) {
@@ -1009,8 +1038,11 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
   //         (Gamma falls along the rows) except in the factorised form, which
   //         is used only where its e^-Gamma stays small ----
   if constexpr (!kChannel) {
-    prep_causal_scalar<OpT, DK, C>(kq, qq, gq, gam0[0], total[0], rlo, active, c4, out, sm, tid,
-                                   lane, wave);
+    OpT* qk_out = r_in == 0 ? static_cast<OpT*>(a.ws_qk) +
+                                  (static_cast<size_t>(bq) * NC + n) * (2 * C * DK)
+                            : nullptr;
+    prep_causal_scalar<OpT, DK, C>(kq, qq, gq, gam0[0], total[0], L, rlo, active, c4, out, qk_out,
+                                   sm, tid, lane, wave);
   } else {
     bool strong = false;
 #pragma unroll
@@ -1136,9 +1168,9 @@ __device__ __forceinline__ void pin_order() {
   if constexpr (kOn) __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename OpT, int DK, int DVS, int C>
+template <typename OpT, int DK, int DVS, int C, bool kRaw>
 struct CarryShape {
-  using Blk = ChunkBlock<OpT, DK, C>;
+  using Blk = ChunkBlock<OpT, DK, C, kRaw>;
   using FK = FragT<OpT, DK>;  // contraction over key channels
   using FC = FragT<OpT, C>;   // contraction over the chunk's tokens
   static constexpr int P = pad_of<OpT>();
@@ -1181,15 +1213,51 @@ struct CarryShape {
 //               writes o.
 enum CarryMode { kCarryFull = 0, kCarryMapN = 1, kCarryMapM = 2 };
 
-template <typename OpT, int DK, int DVS, int C>
+template <typename OpT, int DK, int DVS, int C, bool kRaw>
 struct CarryFrags {
-  using Sh = CarryShape<OpT, DK, DVS, C>;
+  using Sh = CarryShape<OpT, DK, DVS, C, kRaw>;
   typename Sh::FK::T kt[Sh::OPW][Sh::FK::STEPS], qt[Sh::OPW][Sh::FK::STEPS];
   typename Sh::FC::T tb[Sh::OPW][Sh::FC::STEPS], p[Sh::OPW][Sh::FC::STEPS];
   typename Sh::FC::T ke[Sh::SPW][Sh::FC::STEPS];
   OpT v[Sh::OPW][4];  // as loaded (widened to fp32 where used, so the load is not waited for early)
   float gam[Sh::SPW][4];
+  float fk[Sh::OPW][4];  // kRaw: e^Gamma of the four rows of each output tile this lane holds
+  float fq[Sh::OPW];     // kRaw: e^Gamma of the output row this lane stores
 };
+
+// kRaw: the QKRegion of chunk nn of (b, qk head hq).
+template <typename OpT, int DK, int C>
+__device__ __forceinline__ const OpT* qk_region(const PrefillArgs& a, int b, int hq, int nn) {
+  const int NC = (a.T + C - 1) / C;
+  return static_cast<const OpT*>(a.ws_qk) +
+         ((static_cast<size_t>(b) * a.H_qk + hq) * NC + nn) * (2 * C * DK);
+}
+
+// kRaw: the row factors e^Gamma of output tile row-block R in accumulator
+// layout (rows 16 R + 4 (lane / 16) ... + 3) from the block at blk.
+template <typename OpT, int DK, int DVS, int C, bool kRaw>
+__device__ __forceinline__ void carry_load_fk(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const OpT* blk,
+                                              int i, int R, int lane) {
+  using Blk = typename CarryShape<OpT, DK, DVS, C, kRaw>::Blk;
+  const float* fac =
+      reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(blk) + Blk::kFacByte);
+  const float4 f4 = *reinterpret_cast<const float4*>(fac + 16 * R + 4 * (lane >> 4));
+  F.fk[i][0] = f4.x;
+  F.fk[i][1] = f4.y;
+  F.fk[i][2] = f4.z;
+  F.fk[i][3] = f4.w;
+}
+
+// kRaw: the row factor e^Gamma of output row 16 R + lane % 16 (the row this
+// lane stores).
+template <typename OpT, int DK, int DVS, int C, bool kRaw>
+__device__ __forceinline__ void carry_load_fq(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const OpT* blk,
+                                              int i, int R, int lane) {
+  using Blk = typename CarryShape<OpT, DK, DVS, C, kRaw>::Blk;
+  const float* fac =
+      reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(blk) + Blk::kFacByte);
+  F.fq[i] = fac[16 * R + (lane & 15)];
+}
 
 // Issue the loads of chunk nn's fragments for this wave's tiles, by phase:
 // phase c needs Kt, Qt and V; phase d Tb; phase e P, Ke^T and e^Gamma_L.
@@ -1199,11 +1267,11 @@ struct CarryFrags {
 // the worse of the entry path and the loop's own, and a reordered entry (a Qt
 // fragment requested among the last) made every loop trip wait for nearly all
 // of the previous step's loads.
-template <typename OpT, int DK, int DVS, int C, int PHASE, int MODE>
-__device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
+template <typename OpT, int DK, int DVS, int C, bool kRaw, int PHASE, int MODE>
+__device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const PrefillArgs& a,
                                            const unsigned char* ws_head, int nn, int b, int h,
                                            int jb, int wave, int lane) {
-  using Sh = CarryShape<OpT, DK, DVS, C>;
+  using Sh = CarryShape<OpT, DK, DVS, C, kRaw>;
   using Blk = typename Sh::Blk;
   using FK = typename Sh::FK;
   using FC = typename Sh::FC;
@@ -1211,6 +1279,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
   const OpT* blk = reinterpret_cast<const OpT*>(blk_bytes);
   const OpT* vg = static_cast<const OpT*>(a.v);
   const int t0 = nn * C;
+  const OpT* qkr = kRaw ? qk_region<OpT, DK, C>(a, b, h / (a.H_v / a.H_qk), nn) : nullptr;
 #pragma unroll
   for (int i = 0; i < Sh::OPW; ++i) {
     const int t = wave * Sh::OPW + i;
@@ -1219,9 +1288,22 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
       if constexpr (PHASE == 0) {
 #pragma unroll
         for (int s = 0; s < FK::STEPS; ++s) {
-          F.kt[i][s] = FK::load(blk + Blk::kKt, 16 * R, s, lane);
+          if constexpr (kRaw)
+            F.kt[i][s] = FK::load(qkr + QKRegion<OpT, DK, C>::kK, 16 * R, s, lane);
+          else
+            F.kt[i][s] = FK::load(blk + Blk::kKt, 16 * R, s, lane);
           pin_order<Sh::kPinLoads>();
-          if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(blk + Blk::kQt, 16 * R, s, lane);
+          if constexpr (MODE == kCarryFull) {
+            if constexpr (kRaw)
+              F.qt[i][s] = FK::load(qkr + QKRegion<OpT, DK, C>::kQ, 16 * R, s, lane);
+            else
+              F.qt[i][s] = FK::load(blk + Blk::kQt, 16 * R, s, lane);
+          }
+          pin_order<Sh::kPinLoads>();
+        }
+        if constexpr (kRaw) {
+          carry_load_fk<OpT, DK, DVS, C, kRaw>(F, blk, i, R, lane);
+          if constexpr (MODE == kCarryFull) carry_load_fq<OpT, DK, DVS, C, kRaw>(F, blk, i, R, lane);
           pin_order<Sh::kPinLoads>();
         }
         if constexpr (MODE != kCarryMapM) {
@@ -1280,8 +1362,8 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C>& F, const
 }
 
 // V rows of output tile (R, J) of chunk nn, in accumulator layout.
-template <typename OpT, int DK, int DVS, int C>
-__device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C>& F, const PrefillArgs& a,
+template <typename OpT, int DK, int DVS, int C, bool kRaw>
+__device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const PrefillArgs& a,
                                              int nn, int b, int h, int jb, int i, int R, int J,
                                              int lane) {
   // Uniform row base plus 32-bit lane offsets; rows past the end re-read the
@@ -1299,10 +1381,10 @@ __device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C>& F, con
 }
 
 // e^Gamma_L for the rows of state tile row-block I of the block at blk.
-template <typename OpT, int DK, int DVS, int C>
-__device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C>& F, const OpT* blk,
+template <typename OpT, int DK, int DVS, int C, bool kRaw>
+__device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const OpT* blk,
                                                int i, int I, int lane) {
-  using Blk = typename CarryShape<OpT, DK, DVS, C>::Blk;
+  using Blk = typename CarryShape<OpT, DK, DVS, C, kRaw>::Blk;
   const float* gam =
       reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(blk) + Blk::kGammaByte);
   const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
@@ -1312,13 +1394,13 @@ __device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C>& F, c
   F.gam[i][3] = g4.w;
 }
 
-template <typename OpT, int DK, int DVS, int C, int MODE>
-__device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C>& F,
+template <typename OpT, int DK, int DVS, int C, bool kRaw, int MODE>
+__device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C, kRaw>& F,
                                                const PrefillArgs& a, const unsigned char* ws_head,
                                                int nn, int b, int h, int jb, int wave, int lane) {
-  carry_load<OpT, DK, DVS, C, 0, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
-  carry_load<OpT, DK, DVS, C, 1, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
-  carry_load<OpT, DK, DVS, C, 2, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, kRaw, 0, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, kRaw, 1, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, kRaw, 2, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
 }
 
 // One workgroup per (b, h, slice), over the chunks of cr: the state slice
@@ -1326,15 +1408,15 @@ __device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C>& F,
 // in s_dst (not written when it is null).  a.dv is the number of state
 // columns (dk for kCarryMapM).  wg is the workgroup's index among the G that do
 // this work, and sm its LDS (kSmem bytes).
-template <typename OpT, int DK, int DVS, int C, int MODE>
+template <typename OpT, int DK, int DVS, int C, bool kRaw, int MODE>
 __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
                                            const float* s_src, float* s_dst, int wg, int G,
                                            unsigned char* sm) {
-  using Sh = CarryShape<OpT, DK, DVS, C>;
+  using Sh = CarryShape<OpT, DK, DVS, C, kRaw>;
   using Blk = typename Sh::Blk;
   using FK = typename Sh::FK;
   using FC = typename Sh::FC;
-  using Frags = CarryFrags<OpT, DK, DVS, C>;
+  using Frags = CarryFrags<OpT, DK, DVS, C, kRaw>;
   constexpr int LDK = Sh::LDK, LDC = Sh::LDC, DVT = Sh::DVT;
   constexpr int SPW = Sh::SPW, OPW = Sh::OPW, NST = Sh::NST, NOT = Sh::NOT;
 
@@ -1356,6 +1438,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
   const int bh = unit / n_sl;
   const int h = bh % a.H_v;
   const int b = bh / a.H_v;
+  const int hq = h / (a.H_v / a.H_qk);  // qk head of value head h
   const int jb = slice * DVS;
   const int NC = (a.T + C - 1) / C;
 
@@ -1401,6 +1484,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
     const int L = kFull ? C : min(C, a.T - t0);
     const int nx = min(nn + 1, cr.n1 - 1);
     const OpT* nblk = reinterpret_cast<const OpT*>(ws_head + static_cast<size_t>(nx) * Blk::kBytes);
+    const OpT* nqk = kRaw ? qk_region<OpT, DK, C>(a, b, hq, nx) : nullptr;
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -1434,18 +1518,26 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
           // The next chunk's fragments go out one pair per step, each as soon
           // as its registers have been read.
           pin_order<kPin>();  // the reloads below may then reuse the consumed registers
-          F.kt[i][s] = FK::load(nblk + Blk::kKt, 16 * R, s, lane);
-          if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
+          if constexpr (kRaw) {
+            F.kt[i][s] = FK::load(nqk + QKRegion<OpT, DK, C>::kK, 16 * R, s, lane);
+            if constexpr (MODE == kCarryFull)
+              F.qt[i][s] = FK::load(nqk + QKRegion<OpT, DK, C>::kQ, 16 * R, s, lane);
+          } else {
+            F.kt[i][s] = FK::load(nblk + Blk::kKt, 16 * R, s, lane);
+            if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
+          }
           pin_order<kPin>();
         }
         float rv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * R + 4 * (lane >> 4) + e;
-          rv[e] = (r < L ? to_f32(F.v[i][e]) : 0.0f) - ks[e];
+          const float kts = kRaw ? F.fk[i][e] * ks[e] : ks[e];
+          rv[e] = (r < L ? to_f32(F.v[i][e]) : 0.0f) - kts;
         }
         store_tile_t<OpT>(Rt_s, LDC, 16 * J, 16 * R, rv, lane);
-        if constexpr (MODE != kCarryMapM) carry_load_v<OpT, DK, DVS, C>(F, a, nx, b, h, jb, i, R, J, lane);
+        if constexpr (kRaw) carry_load_fk<OpT, DK, DVS, C, kRaw>(F, nblk, i, R, lane);
+        if constexpr (MODE != kCarryMapM) carry_load_v<OpT, DK, DVS, C, kRaw>(F, a, nx, b, h, jb, i, R, J, lane);
       }
     }
     __syncthreads();  // [B2]
@@ -1476,7 +1568,9 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
     // Qt S product (it touches no memory) next to this one, and it puts no wait
     // states between an accumulator written by one shape and read as the
     // addend of the other, which then reads two of its four values too early.
-    constexpr bool kSplitO = FK::KS != FC::KS;
+    // kRaw: Q S is scaled by fQ row by row, so P U goes to accumulators of its
+    // own as well.
+    constexpr bool kSplitO = kRaw || FK::KS != FC::KS;
     f32x4 pacc[OPW];
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
@@ -1513,7 +1607,19 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[i][e] = F.gam[i][e] * sacc[i][e] + t[e];
-        carry_load_gam<OpT, DK, DVS, C>(F, nblk, i, I, lane);
+        carry_load_gam<OpT, DK, DVS, C, kRaw>(F, nblk, i, I, lane);
+      }
+    }
+    // kRaw: O = fQ (Q S) + P U per row; then the next chunk's fQ.
+    if constexpr (kRaw && MODE == kCarryFull) {
+#pragma unroll
+      for (int i = 0; i < OPW; ++i) {
+        const int t = wave * OPW + i;
+        if (NOT % Sh::NW == 0 || t < NOT) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[i][e] = F.fq[i] * oacc[i][e] + pacc[i][e];
+          carry_load_fq<OpT, DK, DVS, C, kRaw>(F, nblk, i, t / DVT, lane);
+        }
       }
     }
     // The o rows go out last, after every load of the step.  On gfx9 stores
@@ -1531,7 +1637,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
         const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
         const int r = 16 * R + (lane & 15);
         OpT* op = obase + (static_cast<unsigned>(r) * rs + 16 * J + 4 * (lane >> 4));
-        if constexpr (kSplitO) {
+        if constexpr (kSplitO && !kRaw) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) oacc[i][e] += pacc[i][e];
         }
@@ -1548,7 +1654,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
   };
 
   Frags F;
-  carry_load_all<OpT, DK, DVS, C, MODE>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
+  carry_load_all<OpT, DK, DVS, C, kRaw, MODE>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
   const int NF = a.T / C;  // full chunks
   const int nf_end = min(cr.n1, NF);
   int nn = cr.n0;
@@ -1596,10 +1702,10 @@ struct CarryJobs {
 
 // kMaps: the launch may hold kCarryMapN / kCarryMapM jobs (instantiated for the one
 // slice width the segmented schedule uses); otherwise every job is kCarryFull.
-template <typename OpT, int DK, int DVS, int C, bool kMaps>
-__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry_kernel(
+template <typename OpT, int DK, int DVS, int C, bool kRaw, bool kMaps>
+__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, kRaw>::NT)) void chunk_carry_kernel(
     PrefillArgs a, CarryJobs J) {
-  __shared__ __attribute__((aligned(16))) unsigned char sm[CarryShape<OpT, DK, DVS, C>::kSmem];
+  __shared__ __attribute__((aligned(16))) unsigned char sm[CarryShape<OpT, DK, DVS, C, kRaw>::kSmem];
   int w = blockIdx.x, k = 0;
   while (k + 1 < J.n && w >= J.job[k].nseg * J.job[k].per) {
     w -= J.job[k].nseg * J.job[k].per;
@@ -1616,15 +1722,15 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C>::NT)) void chunk_carry
   float* dst = jb.dst ? jb.dst + i * jb.dst_stride : nullptr;
   if constexpr (kMaps) {
     if (jb.mode == kCarryMapN) {
-      carry_body<OpT, DK, DVS, C, kCarryMapN>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+      carry_body<OpT, DK, DVS, C, kRaw, kCarryMapN>(ap, cr, src, dst, w % jb.per, jb.per, sm);
       return;
     }
     if (jb.mode == kCarryMapM) {
-      carry_body<OpT, DK, DVS, C, kCarryMapM>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+      carry_body<OpT, DK, DVS, C, kRaw, kCarryMapM>(ap, cr, src, dst, w % jb.per, jb.per, sm);
       return;
     }
   }
-  carry_body<OpT, DK, DVS, C, kCarryFull>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+  carry_body<OpT, DK, DVS, C, kRaw, kCarryFull>(ap, cr, src, dst, w % jb.per, jb.per, sm);
 }
 
 // Start states of segments p0 + 1 ... p1 + 1 of the segmented carry:
@@ -1758,14 +1864,15 @@ __global__ void state_copy_kernel(const float* __restrict__ src, float* __restri
 // dispatch
 // ---------------------------------------------------------------------------
 template <typename OpT, int DK, int C>
-size_t block_bytes() {
-  return ChunkBlock<OpT, DK, C>::kBytes;
+size_t block_bytes(bool raw) {
+  return raw ? ChunkBlock<OpT, DK, C, true>::kBytes : ChunkBlock<OpT, DK, C, false>::kBytes;
 }
 
+// Scalar gates (raw) take the smaller block without Kt and Qt.
 template <typename OpT>
-size_t block_bytes_rt(int dk, int chunk) {
+size_t block_bytes_rt(int dk, int chunk, bool raw) {
 #define GDR_BB(DKV, CV) \
-  if (dk == DKV && chunk == CV) return block_bytes<OpT, DKV, CV>();
+  if (dk == DKV && chunk == CV) return block_bytes<OpT, DKV, CV>(raw);
   GDR_BB(16, 16) GDR_BB(16, 32) GDR_BB(16, 64)
   GDR_BB(32, 16) GDR_BB(32, 32) GDR_BB(32, 64)
   GDR_BB(64, 16) GDR_BB(64, 32) GDR_BB(64, 64)
@@ -1774,23 +1881,23 @@ size_t block_bytes_rt(int dk, int chunk) {
   return 0;
 }
 
-template <typename OpT, int DK, int DVS, int C, bool kMaps>
+template <typename OpT, int DK, int DVS, int C, bool kRaw, bool kMaps>
 hipError_t launch_carry_jobs(const PrefillArgs& a, const CarryJobs& J, hipStream_t stream) {
   unsigned grid = 0;
   for (int k = 0; k < J.n; ++k) grid += static_cast<unsigned>(J.job[k].nseg) * J.job[k].per;
-  hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, kMaps>), dim3(grid),
-                     dim3(CarryShape<OpT, DK, DVS, C>::NT), 0, stream, a, J);
+  hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, kRaw, kMaps>), dim3(grid),
+                     dim3(CarryShape<OpT, DK, DVS, C, kRaw>::NT), 0, stream, a, J);
   return hipGetLastError();
 }
 
 // The plain carry: one job, the whole sequence as one segment.
-template <typename OpT, int DK, int DVS, int C>
+template <typename OpT, int DK, int DVS, int C, bool kRaw>
 hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
   CarryJobs J{};
   J.n = 1;
   J.seg_len = (a.T + C - 1) / C;
   J.job[0] = CarryJob{kCarryFull, 0, 1, a.B * a.H_v * (a.dv / DVS), a.dv, a.state_in, 0, a.state_out, 0};
-  return launch_carry_jobs<OpT, DK, DVS, C, false>(a, J, stream);
+  return launch_carry_jobs<OpT, DK, DVS, C, kRaw, false>(a, J, stream);
 }
 
 // Slice width: the narrowest (from 16 columns) that keeps the number of
@@ -1806,12 +1913,12 @@ int carry_slice_width(const PrefillArgs& a) {
   return dvs;
 }
 
-template <typename OpT, int DK, int C>
+template <typename OpT, int DK, int C, bool kRaw>
 hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
   switch (carry_slice_width(a)) {
-    case 16: return launch_carry<OpT, DK, 16, C>(a, stream);
-    case 32: return launch_carry<OpT, DK, 32, C>(a, stream);
-    default: return launch_carry<OpT, DK, 64, C>(a, stream);
+    case 16: return launch_carry<OpT, DK, 16, C, kRaw>(a, stream);
+    case 32: return launch_carry<OpT, DK, 32, C, kRaw>(a, stream);
+    default: return launch_carry<OpT, DK, 64, C, kRaw>(a, stream);
   }
 }
 
@@ -1880,26 +1987,36 @@ size_t seg_bytes(SegPlan sp, long units, int dk, int dv) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout: the chunk blocks ((b, h)-major, then chunk); at the next
-// 256-byte boundary, the segmented carry's buffers (if it runs).
+// 256-byte boundary, for scalar gates, the QKRegions ((b, qk head)-major, then
+// chunk); at the next 256-byte boundary, the segmented carry's buffers (if it
+// runs).
 struct WsLayout {
-  size_t seg, total;
+  size_t qk, seg, total;
 };
-WsLayout ws_layout(long units, size_t nc, size_t block_bytes, size_t seg) {
+WsLayout ws_layout(long units, size_t nc, size_t block_bytes, size_t qk, size_t seg) {
   const size_t blocks = static_cast<size_t>(units) * nc * block_bytes;
   WsLayout w;
-  w.seg = align256(blocks);
-  w.total = seg ? w.seg + seg : blocks;
+  w.qk = align256(blocks);
+  const size_t end = qk ? w.qk + qk : blocks;
+  w.seg = align256(end);
+  w.total = seg ? w.seg + seg : end;
   return w;
 }
 
-template <typename OpT, int DK, int C>
+// Bytes of the QKRegions of a prefill (scalar gates).
+size_t qk_region_bytes(bool raw, int B, int H_qk, size_t nc, int dk, int chunk, size_t es) {
+  return raw ? static_cast<size_t>(B) * H_qk * nc * 2 * chunk * dk * es : 0;
+}
+
+template <typename OpT, int DK, int C, bool kRaw>
 hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t stream) {
   const long units = static_cast<long>(a.B) * a.H_v;
   const int NC = (a.T + C - 1) / C;
   const int P = sp.P;
   const size_t sv = static_cast<size_t>(units) * DK * a.dv;  // one segment's S or N
   const size_t smm = static_cast<size_t>(units) * DK * DK;   // one segment's M
-  const WsLayout wl = ws_layout(units, NC, ChunkBlock<OpT, DK, C>::kBytes, 1);
+  const WsLayout wl = ws_layout(units, NC, ChunkBlock<OpT, DK, C, kRaw>::kBytes,
+                                qk_region_bytes(kRaw, a.B, a.H_qk, NC, DK, C, sizeof(OpT)), 1);
   float* Sb = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + wl.seg);
   float* Nb = Sb + P * sv;
   float* Mb = Nb + P * sv;
@@ -1912,7 +2029,7 @@ hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t 
   J.job[0] = CarryJob{kCarryFull, 0, 1, per_n, a.dv, a.state_in, 0, Sb + sv, 0};
   J.job[1] = CarryJob{kCarryMapN, 1, P - 2, per_n, a.dv, nullptr, 0, Nb + sv, sv};
   J.job[2] = CarryJob{kCarryMapM, 1, P - 2, per_m, DK, nullptr, 0, Mb + smm, smm};
-  hipError_t err = launch_carry_jobs<OpT, DK, 16, C, true>(a, J, stream);
+  hipError_t err = launch_carry_jobs<OpT, DK, 16, C, kRaw, true>(a, J, stream);
   if (err != hipSuccess) return err;
 
   hipLaunchKernelGGL(carry_scan_kernel<DK>, dim3(static_cast<unsigned>(per_n)), dim3(256), 0,
@@ -1925,7 +2042,7 @@ hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t 
   R.seg_len = sp.seg_len;
   R.job[0] = CarryJob{kCarryFull, 1, P - 2, per_n, a.dv, Sb + sv, sv, nullptr, 0};
   R.job[1] = CarryJob{kCarryFull, P - 1, 1, per_n, a.dv, Sb + (P - 1) * sv, 0, a.state_out, 0};
-  return launch_carry_jobs<OpT, DK, 16, C, false>(a, R, stream);
+  return launch_carry_jobs<OpT, DK, 16, C, kRaw, false>(a, R, stream);
 }
 
 template <typename OpT, int DK, int C>
@@ -1941,13 +2058,24 @@ hipError_t launch_prep(const PrefillArgs& a, ChunkRange cr, hipStream_t stream) 
 }
 
 template <typename OpT, int DK, int C>
-hipError_t launch_dk_c(const PrefillArgs& a, hipStream_t stream) {
-  const ChunkRange all{0, (a.T + C - 1) / C};
+hipError_t launch_dk_c(const PrefillArgs& a0, hipStream_t stream) {
+  const int NC = (a0.T + C - 1) / C;
+  const ChunkRange all{0, NC};
+  PrefillArgs a = a0;
+  if (a.gate != GDR_GATE_CHANNEL) {
+    const WsLayout wl = ws_layout(static_cast<long>(a.B) * a.H_v, NC,
+                                  ChunkBlock<OpT, DK, C, true>::kBytes, 1, 0);
+    a.ws_qk = static_cast<unsigned char*>(a.ws) + wl.qk;
+  }
   const hipError_t err = launch_prep<OpT, DK, C>(a, all, stream);
   if (err != hipSuccess) return err;
   const SegPlan sp = carry_segments(a.B, a.T, a.H_v, DK, a.dv, C);
-  if (sp.P >= 3) return launch_carry_segmented<OpT, DK, C>(a, sp, stream);
-  return launch_carry_any<OpT, DK, C>(a, stream);
+  if (a.gate == GDR_GATE_CHANNEL) {
+    if (sp.P >= 3) return launch_carry_segmented<OpT, DK, C, false>(a, sp, stream);
+    return launch_carry_any<OpT, DK, C, false>(a, stream);
+  }
+  if (sp.P >= 3) return launch_carry_segmented<OpT, DK, C, true>(a, sp, stream);
+  return launch_carry_any<OpT, DK, C, true>(a, stream);
 }
 
 template <typename OpT, int DK>
@@ -1973,13 +2101,18 @@ hipError_t launch_io(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int B, int T, int H_v, int dk, int dv, int chunk, int io_bf16) {
+size_t prefill_workspace_bytes(int B, int T, int H_qk, int H_v, int dk, int dv, int chunk,
+                               int io_bf16, int gate) {
   if (B <= 0 || T <= 0) return 0;
   const size_t nc = (static_cast<size_t>(T) + chunk - 1) / chunk;
-  const size_t bb = io_bf16 ? block_bytes_rt<bf16>(dk, chunk) : block_bytes_rt<float>(dk, chunk);
+  const bool raw = gate != GDR_GATE_CHANNEL;
+  const size_t bb =
+      io_bf16 ? block_bytes_rt<bf16>(dk, chunk, raw) : block_bytes_rt<float>(dk, chunk, raw);
   const SegPlan sp = carry_segments(B, T, H_v, dk, dv, chunk);
   const long units = static_cast<long>(B) * H_v;
-  return ws_layout(units, nc, bb, seg_bytes(sp, units, dk, dv)).total;
+  return ws_layout(units, nc, bb, qk_region_bytes(raw, B, H_qk, nc, dk, chunk, io_bf16 ? 2 : 4),
+                   seg_bytes(sp, units, dk, dv))
+      .total;
 }
 
 // Scratch of the allocation-free prefill entry point: the workspace of one

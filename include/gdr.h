@@ -124,8 +124,11 @@ int gdr_decode_step(const gdr_dims* dims, gdr_dtype io, gdr_gate gate, const voi
 
 /*
  * gdr_prefill_workspace_size -- bytes of device workspace gdr_prefill_chunked
- * needs for these sizes (0 when B or T is 0).  Returns 0 as well for
- * unsupported arguments; gdr_prefill_chunked then reports the reason.
+ * needs for these sizes and this gate kind (0 when B or T is 0).  Returns 0 as
+ * well for unsupported arguments; gdr_prefill_chunked then reports the reason.
+ * Scalar gates need less per value head: with one decay per token the decayed
+ * keys and queries are row scalings of the normalised k and q rows, which are
+ * kept once per qk head.
  */
 size_t gdr_prefill_workspace_size(const gdr_dims* dims, gdr_dtype io, gdr_gate gate);
 

@@ -189,16 +189,28 @@ def _al(x, n):
     return -(-x // n) * n
 
 
-def block_bytes(dk, chunk, es):
+def block_bytes(dk, chunk, es, scalar_gate=False):
     """One (b, h, chunk) block: Kt, Qt, Ke^T (chunk x dk each), Tb and P (chunk x
-    chunk each) in the operand type, then e^Gamma_L (dk fp32), 16-byte aligned."""
+    chunk each) in the operand type, then e^Gamma_L (dk fp32), 16-byte aligned.
+    Scalar gates leave out Kt and Qt (row scalings of the normalised k and q
+    rows, which are stored once per qk head instead) and add one fp32 row factor
+    per chunk row."""
+    if scalar_gate:
+        return _al((chunk * dk + 2 * chunk * chunk) * es + 4 * dk + 4 * chunk, 16)
     return _al((3 * chunk * dk + 2 * chunk * chunk) * es + 4 * dk, 16)
 
 
-def layout_bytes(units, nc, bb, seg=0):
-    """Chunk blocks; the segmented carry's buffers (if any) at the next 256-byte
-    boundary."""
+def qk_bytes(B, H_qk, nc, dk, chunk, es):
+    """Scalar gates: the normalised k and q rows of each (b, qk head, chunk)."""
+    return B * H_qk * nc * 2 * chunk * dk * es
+
+
+def layout_bytes(units, nc, bb, seg=0, qk=0):
+    """Chunk blocks; for scalar gates the qk rows at the next 256-byte boundary;
+    the segmented carry's buffers (if any) at the next 256-byte boundary."""
     end = units * nc * bb
+    if qk:
+        end = _al(end, 256) + qk
     return _al(end, 256) + seg if seg else end
 
 
@@ -211,10 +223,18 @@ def test_workspace_size_query():
     for io, es in ((1, 2), (0, 4)):
         for T, C in ((1, 16), (16, 16), (17, 16), (100, 32), (129, 64)):
             nc = -(-T // C)
-            expect = layout_bytes(units, nc, block_bytes(32, C, es))
             for gate in (0, 1, 2):
+                sg = gate != 0
+                expect = layout_bytes(units, nc, block_bytes(32, C, es, scalar_gate=sg),
+                                      qk=qk_bytes(2, 2, nc, 32, C, es) if sg else 0)
                 assert size(io=io, gate=gate, T=T, chunk=C) == expect, (io, T, C, gate)
     assert size(T=16) == size(T=1) > 0            # one chunk either way
+    # the long prefill's blocks: 66,048 B with a channel gate; 33,536 B with a
+    # scalar one, plus 32 KiB of k and q rows per qk head (two value heads each)
+    assert block_bytes(128, 64, 2) == 66048 and block_bytes(128, 64, 2, True) == 33536
+    two = dict(B=1, T=64, H_qk=1, H_v=2, dk=128, dv=128, chunk=64)
+    assert size(gate=0, **two) == 2 * 66048
+    assert size(gate=1, **two) == size(gate=2, **two) == _al(2 * 33536, 256) + 32768
 
 
 def test_workspace_size_segmented_carry():

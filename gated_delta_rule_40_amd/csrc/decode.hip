@@ -77,13 +77,21 @@ __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void
   constexpr int C4 = Sh::C4, RPT = Sh::RPT, NW = Sh::NW;
   constexpr int NE = (DK + 63) / 64;  // head elements per lane of wave 0
   // Per-row vectors of the head, shared by the C4 lanes of each row group:
-  // normalised k and q, the decay a, and a*k.
-  __shared__ __attribute__((aligned(16))) float kS[DK], qS[DK], dS[DK], akS[DK];
+  // normalised k and q, the decay a, and a*k.  One copy per wave: every wave
+  // builds the whole set, writes only its own copy and reads it after its own
+  // writes have completed, so no workgroup barrier is needed before pass 1 and
+  // no two waves touch the same words.
+  __shared__ __attribute__((aligned(16))) float kS_w[NW][DK], qS_w[NW][DK], dS_w[NW][DK],
+      akS_w[NW][DK];
   __shared__ float4 red[2][NW][C4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  float* const kS = kS_w[wave];
+  float* const qS = qS_w[wave];
+  float* const dS = dS_w[wave];
+  float* const akS = akS_w[wave];
   const int c4 = tid % C4;
   const int rg = tid / C4;
   const int row0 = rg * RPT;
@@ -149,9 +157,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void
   for (int m = 0; m < RPT; ++m) s[m] = tile_load(srs, boff, m * rstep);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Every wave builds the whole head's vectors and writes them to the same
-  // LDS words; the values are identical, and each wave reads only after its
-  // own writes, so no barrier is needed before pass 1.
+  // Every wave builds the whole head's vectors into its own LDS copy.
   if constexpr (kVec) {
     if (vrow < 2) {
       const IoT* e8 = reinterpret_cast<const IoT*>(&rv4);
@@ -299,7 +305,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(IoT) == 4 && !kChannel ? 4 : 5))) void
 
 // Occupancy cap for large grids of whole 128 x 128 tiles with a channel gate,
 // written with plain stores: LDS the kernel does not use, so that at most
-// three workgroups share a CU (160 KiB of LDS over more than 40 KiB each).
+// three workgroups share a CU (160 KiB of LDS over more than 40 KiB each; the
+// kernel's own LDS, 12 KiB at four waves, comes on top).
 // Fewer tiles in flight contend less for the memory system there (graph
 // replay, bf16: B=64 41.5 -> 41.1 us, B=128 80.7 -> 78.8 us).  Smaller grids
 // lose by it (B=16: 9.5 -> 10.9 us), with streaming stores (B=256) it is

@@ -126,20 +126,49 @@ def test_prefill_mixed_mfma_shapes(B, H_qk, H_v, dk, dv, chunk, T):
     assert rel(o, o_ref) < TOL["bf16"] and rel(S, S_ref) < TOL["bf16"]
 
 
+@pytest.mark.parametrize("gate", [synth.GATE_CHANNEL, synth.GATE_SCALAR])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_prefill_without_l2norm(io):
+def test_prefill_without_l2norm(io, gate):
     """l2norm_qk = 0: q and k are used as given, pre-scaled by 1/sqrt(dk) so
-    that |k| ~ 1; ragged against chunk 32, nonzero initial state."""
+    that |k| ~ 1; ragged against chunk 32, nonzero initial state.  With a
+    scalar gate the stored k and q rows are then the inputs as given."""
     require_gpu()
-    case = synth.prefill_case("nol2", 81, 2, 150, 2, 4, 64, 64, 32, io, synth.GATE_CHANNEL,
+    case = synth.prefill_case("nol2", 81 + gate, 2, 150, 2, 4, 64, 64, 32, io, gate,
                               0.01, 0.3, 0.3)
     t = case.tensors
     for name in ("q", "k"):
         x = case.values(name) * np.float32(1.0 / np.sqrt(case.dk))
         t[name] = synth.f32_to_bf16(x) if io == "bf16" else x.astype(np.float32)
-    announce(f"prefill no-l2norm io={io} B=2 T=150 H 2->4 dk=dv=64 chunk=32")
+    announce(f"prefill no-l2norm io={io} gate={gate} B=2 T=150 H 2->4 dk=dv=64 chunk=32")
     o, S = run_prefill(case, l2norm=False)
     o_ref, S_ref = _oracle(case, l2norm=False)
+    print(f"err o={rel(o, o_ref):.3e} S={rel(S, S_ref):.3e}")
+    assert rel(o, o_ref) < TOL[io] and rel(S, S_ref) < TOL[io]
+
+
+# Scalar gates keep the normalised k and q rows once per (b, qk head, chunk),
+# written by the first value head of each qk head and read by all of them.
+# Cases: four, one and three value heads per qk head, every slice width of
+# the carry (16 to 64 columns), the segmented carry, both io dtypes and both
+# scalar gate kinds; outputs NaN-filled beforehand.
+@pytest.mark.parametrize("B,H_qk,H_v,dk,dv,chunk,T,io,gate", [
+    (3, 2, 8, 64, 64, 32, 150, "bf16", synth.GATE_SCALAR),
+    (1, 3, 3, 128, 128, 64, 200, "bf16", synth.GATE_SCALAR_FUSED),
+    (2, 1, 3, 32, 64, 16, 77, "f32", synth.GATE_SCALAR),
+    (2, 8, 32, 128, 128, 64, 130, "bf16", synth.GATE_SCALAR),
+    (4, 16, 32, 128, 128, 64, 130, "bf16", synth.GATE_SCALAR_FUSED),
+    (1, 1, 4, 64, 64, 32, 3000, "bf16", synth.GATE_SCALAR),
+])
+def test_prefill_scalar_gate_shared_qk_rows(B, H_qk, H_v, dk, dv, chunk, T, io, gate):
+    require_gpu()
+    case = synth.prefill_case("sqk", 460 + H_v + T % 97, B, T, H_qk, H_v, dk, dv, chunk, io, gate,
+                              0.01, 0.3, 0.3)
+    segs = carry_segments(B, T, H_v, dk, dv, chunk)
+    announce(f"prefill scalar gate, shared k/q rows: B={B} T={T} H {H_qk}->{H_v} dk={dk} dv={dv} "
+             f"chunk={chunk} io={io} gate={gate} carry segments={segs}")
+    o, S = run_prefill(case, o_fill=float("nan"))
+    o_ref, S_ref = _oracle(case)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
     print(f"err o={rel(o, o_ref):.3e} S={rel(S, S_ref):.3e}")
     assert rel(o, o_ref) < TOL[io] and rel(S, S_ref) < TOL[io]
 

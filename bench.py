@@ -463,7 +463,7 @@ def bench_prefill_segmented(reps=4, warm=1):
 # ---------------------------------------------------------------------------
 # T-sweep: T decode steps against one chunked prefill of the same T tokens
 # ---------------------------------------------------------------------------
-SWEEP_TS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4000)
+SWEEP_TS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4000, 8192, 16384, 32767)
 
 
 def graph_us(fn, reps=5):

@@ -33,7 +33,10 @@
 //   chunk_prep   one workgroup per (b, h, chunk), all chunks in parallel:
 //                everything that does not depend on S -- Kt, Qt, Ke^T, Tb, P
 //                and e^Gamma_L -- written to the caller's workspace, one
-//                disjoint block per (b, h, chunk).
+//                disjoint block per (b, h, chunk).  With a scalar gate Kt
+//                and Qt are row scalings: the block holds the row factors
+//                instead, and the normalised k and q rows go once per
+//                (b, qk head, chunk) to a region of their own.
 //   chunk_carry  one workgroup per (b, h, slice of DVS state columns), walking
 //                the chunks in order with its state slice held in MFMA
 //                accumulators; the columns of S are independent, so slices
@@ -1153,8 +1156,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, Chu
 // holds is an A operand of some product, and each wave reads exactly the rows
 // of them its tiles need straight from global memory into registers (each
 // fragment one contiguous read, the block being in fragment order), ahead of
-// their use.  LDS only carries what the waves exchange: S^T, R^T and U^T.
-// Per chunk, three barriers:
+// their use (scalar gates: the Kt and Qt fragments from the qk head's region
+// of normalised rows, the products then scaled row by row).  LDS only
+// carries what the waves exchange: S^T, R^T and U^T.  Per chunk, three
+// barriers:
 //   [B1]  S^T (operand type) written
 //   c:    R = V - Kt S (to LDS, transposed), O = Qt S (registers)      [B2]
 //   d:    U = Tb R (to LDS, transposed)                                  [B3]

@@ -172,24 +172,25 @@ struct FragT {
 // in fragment order (FragT::slot_row / slot_col): Kt and Qt for a
 // contraction over DK, the others over C.
 //
-// kRaw (scalar gates): with one decay per row, Kt = diag(e^Gamma) K and
+// kScalarGate (scalar gates): with one decay per row, Kt = diag(e^Gamma) K and
 // Qt = diag(e^Gamma) Q are row scalings of the normalised k and q rows, which
 // do not depend on the value head.  The block of a value head then leaves Kt
 // and Qt out and holds the row factor e^Gamma_r instead (0 on the rows past
 // the end of a ragged last chunk); the normalised rows are stored once per
 // (b, qk head, chunk) in a QKRegion, and the carry scales its products row by
 // row.  With two value heads per qk head that is a quarter fewer bytes.
-template <typename OpT, int DK, int C, bool kRaw>
+template <typename OpT, int DK, int C, bool kScalarGate>
 struct ChunkBlock {
-  static constexpr int kKt = 0;                          // [C][DK]  K e^Gamma (not kRaw)
-  static constexpr int kQt = C * DK;                     // [C][DK]  Q e^Gamma (not kRaw)
-  static constexpr int kKeT = kRaw ? 0 : 2 * C * DK;     // [DK][C]  (K e^(Gamma_L - Gamma))^T
-  static constexpr int kTb = kKeT + C * DK;              // [C][C]   (I + A)^-1 diag(beta)
-  static constexpr int kP = kTb + C * C;                 // [C][C]   lower(Q K^T o D)
+  static constexpr int kKt = 0;                         // [C][DK] K e^Gamma (channel gates)
+  static constexpr int kQt = C * DK;                    // [C][DK] Q e^Gamma (channel gates)
+  static constexpr int kKeT = kScalarGate ? 0 : 2 * C * DK;  // [DK][C] (K e^(Gamma_L - Gamma))^T
+  static constexpr int kTb = kKeT + C * DK;             // [C][C]  (I + A)^-1 diag(beta)
+  static constexpr int kP = kTb + C * C;                // [C][C]  lower(Q K^T o D)
   static constexpr int kOpElems = kP + C * C;
   static constexpr size_t kGammaByte = static_cast<size_t>(kOpElems) * sizeof(OpT);  // [DK] f32
-  static constexpr size_t kFacByte = kGammaByte + DK * sizeof(float);  // kRaw: e^Gamma [C] f32
-  static constexpr size_t kBytes = (kFacByte + (kRaw ? C * sizeof(float) : 0) + 15) / 16 * 16;
+  static constexpr size_t kFacByte = kGammaByte + DK * sizeof(float);  // scalar: e^Gamma [C] f32
+  static constexpr size_t kBytes =
+      (kFacByte + (kScalarGate ? C * sizeof(float) : 0) + 15) / 16 * 16;
 };
 
 // Scalar gates: the normalised k rows and q rows of one (b, qk head, chunk),
@@ -1173,9 +1174,9 @@ __device__ __forceinline__ void pin_order() {
   if constexpr (kOn) __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename OpT, int DK, int DVS, int C, bool kRaw>
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate>
 struct CarryShape {
-  using Blk = ChunkBlock<OpT, DK, C, kRaw>;
+  using Blk = ChunkBlock<OpT, DK, C, kScalarGate>;
   using FK = FragT<OpT, DK>;  // contraction over key channels
   using FC = FragT<OpT, C>;   // contraction over the chunk's tokens
   static constexpr int P = pad_of<OpT>();
@@ -1218,19 +1219,19 @@ struct CarryShape {
 //               writes o.
 enum CarryMode { kCarryFull = 0, kCarryMapN = 1, kCarryMapM = 2 };
 
-template <typename OpT, int DK, int DVS, int C, bool kRaw>
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate>
 struct CarryFrags {
-  using Sh = CarryShape<OpT, DK, DVS, C, kRaw>;
+  using Sh = CarryShape<OpT, DK, DVS, C, kScalarGate>;
   typename Sh::FK::T kt[Sh::OPW][Sh::FK::STEPS], qt[Sh::OPW][Sh::FK::STEPS];
   typename Sh::FC::T tb[Sh::OPW][Sh::FC::STEPS], p[Sh::OPW][Sh::FC::STEPS];
   typename Sh::FC::T ke[Sh::SPW][Sh::FC::STEPS];
   OpT v[Sh::OPW][4];  // as loaded (widened to fp32 where used, so the load is not waited for early)
   float gam[Sh::SPW][4];
-  float fk[Sh::OPW][4];  // kRaw: e^Gamma of the four rows of each output tile this lane holds
-  float fq[Sh::OPW];     // kRaw: e^Gamma of the output row this lane stores
+  float fk[Sh::OPW][4];  // scalar gates: e^Gamma of the four rows of each output tile of the lane
+  float fq[Sh::OPW];     // scalar gates: e^Gamma of the output row this lane stores
 };
 
-// kRaw: the QKRegion of chunk nn of (b, qk head hq).
+// kScalarGate: the QKRegion of chunk nn of (b, qk head hq).
 template <typename OpT, int DK, int C>
 __device__ __forceinline__ const OpT* qk_region(const PrefillArgs& a, int b, int hq, int nn) {
   const int NC = (a.T + C - 1) / C;
@@ -1238,12 +1239,12 @@ __device__ __forceinline__ const OpT* qk_region(const PrefillArgs& a, int b, int
          ((static_cast<size_t>(b) * a.H_qk + hq) * NC + nn) * (2 * C * DK);
 }
 
-// kRaw: the row factors e^Gamma of output tile row-block R in accumulator
+// kScalarGate: the row factors e^Gamma of output tile row-block R in accumulator
 // layout (rows 16 R + 4 (lane / 16) ... + 3) from the block at blk.
-template <typename OpT, int DK, int DVS, int C, bool kRaw>
-__device__ __forceinline__ void carry_load_fk(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const OpT* blk,
-                                              int i, int R, int lane) {
-  using Blk = typename CarryShape<OpT, DK, DVS, C, kRaw>::Blk;
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate>
+__device__ __forceinline__ void carry_load_fk(CarryFrags<OpT, DK, DVS, C, kScalarGate>& F,
+                                              const OpT* blk, int i, int R, int lane) {
+  using Blk = typename CarryShape<OpT, DK, DVS, C, kScalarGate>::Blk;
   const float* fac =
       reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(blk) + Blk::kFacByte);
   const float4 f4 = *reinterpret_cast<const float4*>(fac + 16 * R + 4 * (lane >> 4));
@@ -1253,12 +1254,12 @@ __device__ __forceinline__ void carry_load_fk(CarryFrags<OpT, DK, DVS, C, kRaw>&
   F.fk[i][3] = f4.w;
 }
 
-// kRaw: the row factor e^Gamma of output row 16 R + lane % 16 (the row this
+// kScalarGate: the row factor e^Gamma of output row 16 R + lane % 16 (the row this
 // lane stores).
-template <typename OpT, int DK, int DVS, int C, bool kRaw>
-__device__ __forceinline__ void carry_load_fq(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const OpT* blk,
-                                              int i, int R, int lane) {
-  using Blk = typename CarryShape<OpT, DK, DVS, C, kRaw>::Blk;
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate>
+__device__ __forceinline__ void carry_load_fq(CarryFrags<OpT, DK, DVS, C, kScalarGate>& F,
+                                              const OpT* blk, int i, int R, int lane) {
+  using Blk = typename CarryShape<OpT, DK, DVS, C, kScalarGate>::Blk;
   const float* fac =
       reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(blk) + Blk::kFacByte);
   F.fq[i] = fac[16 * R + (lane & 15)];
@@ -1272,11 +1273,11 @@ __device__ __forceinline__ void carry_load_fq(CarryFrags<OpT, DK, DVS, C, kRaw>&
 // the worse of the entry path and the loop's own, and a reordered entry (a Qt
 // fragment requested among the last) made every loop trip wait for nearly all
 // of the previous step's loads.
-template <typename OpT, int DK, int DVS, int C, bool kRaw, int PHASE, int MODE>
-__device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const PrefillArgs& a,
-                                           const unsigned char* ws_head, int nn, int b, int h,
-                                           int jb, int wave, int lane) {
-  using Sh = CarryShape<OpT, DK, DVS, C, kRaw>;
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate, int PHASE, int MODE>
+__device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C, kScalarGate>& F,
+                                           const PrefillArgs& a, const unsigned char* ws_head,
+                                           int nn, int b, int h, int jb, int wave, int lane) {
+  using Sh = CarryShape<OpT, DK, DVS, C, kScalarGate>;
   using Blk = typename Sh::Blk;
   using FK = typename Sh::FK;
   using FC = typename Sh::FC;
@@ -1284,7 +1285,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C, kRaw>& F,
   const OpT* blk = reinterpret_cast<const OpT*>(blk_bytes);
   const OpT* vg = static_cast<const OpT*>(a.v);
   const int t0 = nn * C;
-  const OpT* qkr = kRaw ? qk_region<OpT, DK, C>(a, b, h / (a.H_v / a.H_qk), nn) : nullptr;
+  const OpT* qkr = kScalarGate ? qk_region<OpT, DK, C>(a, b, h / (a.H_v / a.H_qk), nn) : nullptr;
 #pragma unroll
   for (int i = 0; i < Sh::OPW; ++i) {
     const int t = wave * Sh::OPW + i;
@@ -1293,22 +1294,23 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C, kRaw>& F,
       if constexpr (PHASE == 0) {
 #pragma unroll
         for (int s = 0; s < FK::STEPS; ++s) {
-          if constexpr (kRaw)
+          if constexpr (kScalarGate)
             F.kt[i][s] = FK::load(qkr + QKRegion<OpT, DK, C>::kK, 16 * R, s, lane);
           else
             F.kt[i][s] = FK::load(blk + Blk::kKt, 16 * R, s, lane);
           pin_order<Sh::kPinLoads>();
           if constexpr (MODE == kCarryFull) {
-            if constexpr (kRaw)
+            if constexpr (kScalarGate)
               F.qt[i][s] = FK::load(qkr + QKRegion<OpT, DK, C>::kQ, 16 * R, s, lane);
             else
               F.qt[i][s] = FK::load(blk + Blk::kQt, 16 * R, s, lane);
           }
           pin_order<Sh::kPinLoads>();
         }
-        if constexpr (kRaw) {
-          carry_load_fk<OpT, DK, DVS, C, kRaw>(F, blk, i, R, lane);
-          if constexpr (MODE == kCarryFull) carry_load_fq<OpT, DK, DVS, C, kRaw>(F, blk, i, R, lane);
+        if constexpr (kScalarGate) {
+          carry_load_fk<OpT, DK, DVS, C, kScalarGate>(F, blk, i, R, lane);
+          if constexpr (MODE == kCarryFull)
+            carry_load_fq<OpT, DK, DVS, C, kScalarGate>(F, blk, i, R, lane);
           pin_order<Sh::kPinLoads>();
         }
         if constexpr (MODE != kCarryMapM) {
@@ -1367,10 +1369,10 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C, kRaw>& F,
 }
 
 // V rows of output tile (R, J) of chunk nn, in accumulator layout.
-template <typename OpT, int DK, int DVS, int C, bool kRaw>
-__device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const PrefillArgs& a,
-                                             int nn, int b, int h, int jb, int i, int R, int J,
-                                             int lane) {
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate>
+__device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C, kScalarGate>& F,
+                                             const PrefillArgs& a, int nn, int b, int h, int jb,
+                                             int i, int R, int J, int lane) {
   // Uniform row base plus 32-bit lane offsets; rows past the end re-read the
   // last row and are zeroed when used.
   const int t0 = nn * C;
@@ -1386,10 +1388,10 @@ __device__ __forceinline__ void carry_load_v(CarryFrags<OpT, DK, DVS, C, kRaw>& 
 }
 
 // e^Gamma_L for the rows of state tile row-block I of the block at blk.
-template <typename OpT, int DK, int DVS, int C, bool kRaw>
-__device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C, kRaw>& F, const OpT* blk,
-                                               int i, int I, int lane) {
-  using Blk = typename CarryShape<OpT, DK, DVS, C, kRaw>::Blk;
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate>
+__device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C, kScalarGate>& F,
+                                               const OpT* blk, int i, int I, int lane) {
+  using Blk = typename CarryShape<OpT, DK, DVS, C, kScalarGate>::Blk;
   const float* gam =
       reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(blk) + Blk::kGammaByte);
   const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * I + 4 * (lane >> 4));
@@ -1399,13 +1401,13 @@ __device__ __forceinline__ void carry_load_gam(CarryFrags<OpT, DK, DVS, C, kRaw>
   F.gam[i][3] = g4.w;
 }
 
-template <typename OpT, int DK, int DVS, int C, bool kRaw, int MODE>
-__device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C, kRaw>& F,
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate, int MODE>
+__device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C, kScalarGate>& F,
                                                const PrefillArgs& a, const unsigned char* ws_head,
                                                int nn, int b, int h, int jb, int wave, int lane) {
-  carry_load<OpT, DK, DVS, C, kRaw, 0, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
-  carry_load<OpT, DK, DVS, C, kRaw, 1, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
-  carry_load<OpT, DK, DVS, C, kRaw, 2, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, kScalarGate, 0, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, kScalarGate, 1, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
+  carry_load<OpT, DK, DVS, C, kScalarGate, 2, MODE>(F, a, ws_head, nn, b, h, jb, wave, lane);
 }
 
 // One workgroup per (b, h, slice), over the chunks of cr: the state slice
@@ -1413,15 +1415,15 @@ __device__ __forceinline__ void carry_load_all(CarryFrags<OpT, DK, DVS, C, kRaw>
 // in s_dst (not written when it is null).  a.dv is the number of state
 // columns (dk for kCarryMapM).  wg is the workgroup's index among the G that do
 // this work, and sm its LDS (kSmem bytes).
-template <typename OpT, int DK, int DVS, int C, bool kRaw, int MODE>
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate, int MODE>
 __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
                                            const float* s_src, float* s_dst, int wg, int G,
                                            unsigned char* sm) {
-  using Sh = CarryShape<OpT, DK, DVS, C, kRaw>;
+  using Sh = CarryShape<OpT, DK, DVS, C, kScalarGate>;
   using Blk = typename Sh::Blk;
   using FK = typename Sh::FK;
   using FC = typename Sh::FC;
-  using Frags = CarryFrags<OpT, DK, DVS, C, kRaw>;
+  using Frags = CarryFrags<OpT, DK, DVS, C, kScalarGate>;
   constexpr int LDK = Sh::LDK, LDC = Sh::LDC, DVT = Sh::DVT;
   constexpr int SPW = Sh::SPW, OPW = Sh::OPW, NST = Sh::NST, NOT = Sh::NOT;
 
@@ -1489,7 +1491,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
     const int L = kFull ? C : min(C, a.T - t0);
     const int nx = min(nn + 1, cr.n1 - 1);
     const OpT* nblk = reinterpret_cast<const OpT*>(ws_head + static_cast<size_t>(nx) * Blk::kBytes);
-    const OpT* nqk = kRaw ? qk_region<OpT, DK, C>(a, b, hq, nx) : nullptr;
+    const OpT* nqk = kScalarGate ? qk_region<OpT, DK, C>(a, b, hq, nx) : nullptr;
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -1523,13 +1525,14 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
           // The next chunk's fragments go out one pair per step, each as soon
           // as its registers have been read.
           pin_order<kPin>();  // the reloads below may then reuse the consumed registers
-          if constexpr (kRaw) {
+          if constexpr (kScalarGate) {
             F.kt[i][s] = FK::load(nqk + QKRegion<OpT, DK, C>::kK, 16 * R, s, lane);
             if constexpr (MODE == kCarryFull)
               F.qt[i][s] = FK::load(nqk + QKRegion<OpT, DK, C>::kQ, 16 * R, s, lane);
           } else {
             F.kt[i][s] = FK::load(nblk + Blk::kKt, 16 * R, s, lane);
-            if constexpr (MODE == kCarryFull) F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
+            if constexpr (MODE == kCarryFull)
+              F.qt[i][s] = FK::load(nblk + Blk::kQt, 16 * R, s, lane);
           }
           pin_order<kPin>();
         }
@@ -1537,12 +1540,13 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * R + 4 * (lane >> 4) + e;
-          const float kts = kRaw ? F.fk[i][e] * ks[e] : ks[e];
+          const float kts = kScalarGate ? F.fk[i][e] * ks[e] : ks[e];
           rv[e] = (r < L ? to_f32(F.v[i][e]) : 0.0f) - kts;
         }
         store_tile_t<OpT>(Rt_s, LDC, 16 * J, 16 * R, rv, lane);
-        if constexpr (kRaw) carry_load_fk<OpT, DK, DVS, C, kRaw>(F, nblk, i, R, lane);
-        if constexpr (MODE != kCarryMapM) carry_load_v<OpT, DK, DVS, C, kRaw>(F, a, nx, b, h, jb, i, R, J, lane);
+        if constexpr (kScalarGate) carry_load_fk<OpT, DK, DVS, C, kScalarGate>(F, nblk, i, R, lane);
+        if constexpr (MODE != kCarryMapM)
+          carry_load_v<OpT, DK, DVS, C, kScalarGate>(F, a, nx, b, h, jb, i, R, J, lane);
       }
     }
     __syncthreads();  // [B2]
@@ -1573,9 +1577,9 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
     // Qt S product (it touches no memory) next to this one, and it puts no wait
     // states between an accumulator written by one shape and read as the
     // addend of the other, which then reads two of its four values too early.
-    // kRaw: Q S is scaled by fQ row by row, so P U goes to accumulators of its
-    // own as well.
-    constexpr bool kSplitO = kRaw || FK::KS != FC::KS;
+    // Scalar gates: Q S is scaled by e^Gamma row by row, so P U goes to
+    // accumulators of its own as well.
+    constexpr bool kSplitO = kScalarGate || FK::KS != FC::KS;
     f32x4 pacc[OPW];
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
@@ -1612,18 +1616,18 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[i][e] = F.gam[i][e] * sacc[i][e] + t[e];
-        carry_load_gam<OpT, DK, DVS, C, kRaw>(F, nblk, i, I, lane);
+        carry_load_gam<OpT, DK, DVS, C, kScalarGate>(F, nblk, i, I, lane);
       }
     }
-    // kRaw: O = fQ (Q S) + P U per row; then the next chunk's fQ.
-    if constexpr (kRaw && MODE == kCarryFull) {
+    // Scalar gates: O = e^Gamma (Q S) + P U per row; then the next chunk's factors.
+    if constexpr (kScalarGate && MODE == kCarryFull) {
 #pragma unroll
       for (int i = 0; i < OPW; ++i) {
         const int t = wave * OPW + i;
         if (NOT % Sh::NW == 0 || t < NOT) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) oacc[i][e] = F.fq[i] * oacc[i][e] + pacc[i][e];
-          carry_load_fq<OpT, DK, DVS, C, kRaw>(F, nblk, i, t / DVT, lane);
+          carry_load_fq<OpT, DK, DVS, C, kScalarGate>(F, nblk, i, t / DVT, lane);
         }
       }
     }
@@ -1642,7 +1646,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
         const unsigned rs = static_cast<unsigned>(a.H_v) * a.dv;
         const int r = 16 * R + (lane & 15);
         OpT* op = obase + (static_cast<unsigned>(r) * rs + 16 * J + 4 * (lane >> 4));
-        if constexpr (kSplitO && !kRaw) {
+        if constexpr (kSplitO && !kScalarGate) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) oacc[i][e] += pacc[i][e];
         }
@@ -1659,7 +1663,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
   };
 
   Frags F;
-  carry_load_all<OpT, DK, DVS, C, kRaw, MODE>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
+  carry_load_all<OpT, DK, DVS, C, kScalarGate, MODE>(F, a, ws_head, cr.n0, b, h, jb, wave, lane);
   const int NF = a.T / C;  // full chunks
   const int nf_end = min(cr.n1, NF);
   int nn = cr.n0;
@@ -1707,10 +1711,11 @@ struct CarryJobs {
 
 // kMaps: the launch may hold kCarryMapN / kCarryMapM jobs (instantiated for the one
 // slice width the segmented schedule uses); otherwise every job is kCarryFull.
-template <typename OpT, int DK, int DVS, int C, bool kRaw, bool kMaps>
-__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, kRaw>::NT)) void chunk_carry_kernel(
-    PrefillArgs a, CarryJobs J) {
-  __shared__ __attribute__((aligned(16))) unsigned char sm[CarryShape<OpT, DK, DVS, C, kRaw>::kSmem];
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate, bool kMaps>
+__global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, kScalarGate>::NT)) void
+chunk_carry_kernel(PrefillArgs a, CarryJobs J) {
+  using Sh = CarryShape<OpT, DK, DVS, C, kScalarGate>;
+  __shared__ __attribute__((aligned(16))) unsigned char sm[Sh::kSmem];
   int w = blockIdx.x, k = 0;
   while (k + 1 < J.n && w >= J.job[k].nseg * J.job[k].per) {
     w -= J.job[k].nseg * J.job[k].per;
@@ -1727,15 +1732,17 @@ __global__ __launch_bounds__((CarryShape<OpT, DK, DVS, C, kRaw>::NT)) void chunk
   float* dst = jb.dst ? jb.dst + i * jb.dst_stride : nullptr;
   if constexpr (kMaps) {
     if (jb.mode == kCarryMapN) {
-      carry_body<OpT, DK, DVS, C, kRaw, kCarryMapN>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+      carry_body<OpT, DK, DVS, C, kScalarGate, kCarryMapN>(ap, cr, src, dst, w % jb.per, jb.per,
+                                                           sm);
       return;
     }
     if (jb.mode == kCarryMapM) {
-      carry_body<OpT, DK, DVS, C, kRaw, kCarryMapM>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+      carry_body<OpT, DK, DVS, C, kScalarGate, kCarryMapM>(ap, cr, src, dst, w % jb.per, jb.per,
+                                                           sm);
       return;
     }
   }
-  carry_body<OpT, DK, DVS, C, kRaw, kCarryFull>(ap, cr, src, dst, w % jb.per, jb.per, sm);
+  carry_body<OpT, DK, DVS, C, kScalarGate, kCarryFull>(ap, cr, src, dst, w % jb.per, jb.per, sm);
 }
 
 // Start states of segments p0 + 1 ... p1 + 1 of the segmented carry:
@@ -1869,15 +1876,15 @@ __global__ void state_copy_kernel(const float* __restrict__ src, float* __restri
 // dispatch
 // ---------------------------------------------------------------------------
 template <typename OpT, int DK, int C>
-size_t block_bytes(bool raw) {
-  return raw ? ChunkBlock<OpT, DK, C, true>::kBytes : ChunkBlock<OpT, DK, C, false>::kBytes;
+size_t block_bytes(bool scalar_gate) {
+  return scalar_gate ? ChunkBlock<OpT, DK, C, true>::kBytes : ChunkBlock<OpT, DK, C, false>::kBytes;
 }
 
-// Scalar gates (raw) take the smaller block without Kt and Qt.
+// Scalar gates take the smaller block without Kt and Qt.
 template <typename OpT>
-size_t block_bytes_rt(int dk, int chunk, bool raw) {
+size_t block_bytes_rt(int dk, int chunk, bool scalar_gate) {
 #define GDR_BB(DKV, CV) \
-  if (dk == DKV && chunk == CV) return block_bytes<OpT, DKV, CV>(raw);
+  if (dk == DKV && chunk == CV) return block_bytes<OpT, DKV, CV>(scalar_gate);
   GDR_BB(16, 16) GDR_BB(16, 32) GDR_BB(16, 64)
   GDR_BB(32, 16) GDR_BB(32, 32) GDR_BB(32, 64)
   GDR_BB(64, 16) GDR_BB(64, 32) GDR_BB(64, 64)
@@ -1886,23 +1893,23 @@ size_t block_bytes_rt(int dk, int chunk, bool raw) {
   return 0;
 }
 
-template <typename OpT, int DK, int DVS, int C, bool kRaw, bool kMaps>
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate, bool kMaps>
 hipError_t launch_carry_jobs(const PrefillArgs& a, const CarryJobs& J, hipStream_t stream) {
   unsigned grid = 0;
   for (int k = 0; k < J.n; ++k) grid += static_cast<unsigned>(J.job[k].nseg) * J.job[k].per;
-  hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, kRaw, kMaps>), dim3(grid),
-                     dim3(CarryShape<OpT, DK, DVS, C, kRaw>::NT), 0, stream, a, J);
+  hipLaunchKernelGGL((chunk_carry_kernel<OpT, DK, DVS, C, kScalarGate, kMaps>), dim3(grid),
+                     dim3(CarryShape<OpT, DK, DVS, C, kScalarGate>::NT), 0, stream, a, J);
   return hipGetLastError();
 }
 
 // The plain carry: one job, the whole sequence as one segment.
-template <typename OpT, int DK, int DVS, int C, bool kRaw>
+template <typename OpT, int DK, int DVS, int C, bool kScalarGate>
 hipError_t launch_carry(const PrefillArgs& a, hipStream_t stream) {
   CarryJobs J{};
   J.n = 1;
   J.seg_len = (a.T + C - 1) / C;
   J.job[0] = CarryJob{kCarryFull, 0, 1, a.B * a.H_v * (a.dv / DVS), a.dv, a.state_in, 0, a.state_out, 0};
-  return launch_carry_jobs<OpT, DK, DVS, C, kRaw, false>(a, J, stream);
+  return launch_carry_jobs<OpT, DK, DVS, C, kScalarGate, false>(a, J, stream);
 }
 
 // Slice width: the narrowest (from 16 columns) that keeps the number of
@@ -1918,12 +1925,12 @@ int carry_slice_width(const PrefillArgs& a) {
   return dvs;
 }
 
-template <typename OpT, int DK, int C, bool kRaw>
+template <typename OpT, int DK, int C, bool kScalarGate>
 hipError_t launch_carry_any(const PrefillArgs& a, hipStream_t stream) {
   switch (carry_slice_width(a)) {
-    case 16: return launch_carry<OpT, DK, 16, C, kRaw>(a, stream);
-    case 32: return launch_carry<OpT, DK, 32, C, kRaw>(a, stream);
-    default: return launch_carry<OpT, DK, 64, C, kRaw>(a, stream);
+    case 16: return launch_carry<OpT, DK, 16, C, kScalarGate>(a, stream);
+    case 32: return launch_carry<OpT, DK, 32, C, kScalarGate>(a, stream);
+    default: return launch_carry<OpT, DK, 64, C, kScalarGate>(a, stream);
   }
 }
 
@@ -2009,19 +2016,19 @@ WsLayout ws_layout(long units, size_t nc, size_t block_bytes, size_t qk, size_t 
 }
 
 // Bytes of the QKRegions of a prefill (scalar gates).
-size_t qk_region_bytes(bool raw, int B, int H_qk, size_t nc, int dk, int chunk, size_t es) {
-  return raw ? static_cast<size_t>(B) * H_qk * nc * 2 * chunk * dk * es : 0;
+size_t qk_region_bytes(bool scalar_gate, int B, int H_qk, size_t nc, int dk, int chunk, size_t es) {
+  return scalar_gate ? static_cast<size_t>(B) * H_qk * nc * 2 * chunk * dk * es : 0;
 }
 
-template <typename OpT, int DK, int C, bool kRaw>
+template <typename OpT, int DK, int C, bool kScalarGate>
 hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t stream) {
   const long units = static_cast<long>(a.B) * a.H_v;
   const int NC = (a.T + C - 1) / C;
   const int P = sp.P;
   const size_t sv = static_cast<size_t>(units) * DK * a.dv;  // one segment's S or N
   const size_t smm = static_cast<size_t>(units) * DK * DK;   // one segment's M
-  const WsLayout wl = ws_layout(units, NC, ChunkBlock<OpT, DK, C, kRaw>::kBytes,
-                                qk_region_bytes(kRaw, a.B, a.H_qk, NC, DK, C, sizeof(OpT)), 1);
+  const size_t qk = qk_region_bytes(kScalarGate, a.B, a.H_qk, NC, DK, C, sizeof(OpT));
+  const WsLayout wl = ws_layout(units, NC, ChunkBlock<OpT, DK, C, kScalarGate>::kBytes, qk, 1);
   float* Sb = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + wl.seg);
   float* Nb = Sb + P * sv;
   float* Mb = Nb + P * sv;
@@ -2034,7 +2041,7 @@ hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t 
   J.job[0] = CarryJob{kCarryFull, 0, 1, per_n, a.dv, a.state_in, 0, Sb + sv, 0};
   J.job[1] = CarryJob{kCarryMapN, 1, P - 2, per_n, a.dv, nullptr, 0, Nb + sv, sv};
   J.job[2] = CarryJob{kCarryMapM, 1, P - 2, per_m, DK, nullptr, 0, Mb + smm, smm};
-  hipError_t err = launch_carry_jobs<OpT, DK, 16, C, kRaw, true>(a, J, stream);
+  hipError_t err = launch_carry_jobs<OpT, DK, 16, C, kScalarGate, true>(a, J, stream);
   if (err != hipSuccess) return err;
 
   hipLaunchKernelGGL(carry_scan_kernel<DK>, dim3(static_cast<unsigned>(per_n)), dim3(256), 0,
@@ -2047,7 +2054,7 @@ hipError_t launch_carry_segmented(const PrefillArgs& a, SegPlan sp, hipStream_t 
   R.seg_len = sp.seg_len;
   R.job[0] = CarryJob{kCarryFull, 1, P - 2, per_n, a.dv, Sb + sv, sv, nullptr, 0};
   R.job[1] = CarryJob{kCarryFull, P - 1, 1, per_n, a.dv, Sb + (P - 1) * sv, 0, a.state_out, 0};
-  return launch_carry_jobs<OpT, DK, 16, C, kRaw, false>(a, R, stream);
+  return launch_carry_jobs<OpT, DK, 16, C, kScalarGate, false>(a, R, stream);
 }
 
 template <typename OpT, int DK, int C>
@@ -2110,14 +2117,13 @@ size_t prefill_workspace_bytes(int B, int T, int H_qk, int H_v, int dk, int dv, 
                                int io_bf16, int gate) {
   if (B <= 0 || T <= 0) return 0;
   const size_t nc = (static_cast<size_t>(T) + chunk - 1) / chunk;
-  const bool raw = gate != GDR_GATE_CHANNEL;
-  const size_t bb =
-      io_bf16 ? block_bytes_rt<bf16>(dk, chunk, raw) : block_bytes_rt<float>(dk, chunk, raw);
+  const bool scalar_gate = gate != GDR_GATE_CHANNEL;
+  const size_t bb = io_bf16 ? block_bytes_rt<bf16>(dk, chunk, scalar_gate)
+                            : block_bytes_rt<float>(dk, chunk, scalar_gate);
+  const size_t qk = qk_region_bytes(scalar_gate, B, H_qk, nc, dk, chunk, io_bf16 ? 2 : 4);
   const SegPlan sp = carry_segments(B, T, H_v, dk, dv, chunk);
   const long units = static_cast<long>(B) * H_v;
-  return ws_layout(units, nc, bb, qk_region_bytes(raw, B, H_qk, nc, dk, chunk, io_bf16 ? 2 : 4),
-                   seg_bytes(sp, units, dk, dv))
-      .total;
+  return ws_layout(units, nc, bb, qk, seg_bytes(sp, units, dk, dv)).total;
 }
 
 // Scratch of the allocation-free prefill entry point: the workspace of one

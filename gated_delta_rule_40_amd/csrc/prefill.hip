@@ -2076,8 +2076,8 @@ hipError_t launch_dk_c(const PrefillArgs& a0, hipStream_t stream) {
   PrefillArgs a = a0;
   if (a.gate != GDR_GATE_CHANNEL) {
     const WsLayout wl = ws_layout(static_cast<long>(a.B) * a.H_v, NC,
-                                  ChunkBlock<OpT, DK, C, true>::kBytes, 1, 0);
-    a.ws_qk = static_cast<unsigned char*>(a.ws) + wl.qk;
+                                  ChunkBlock<OpT, DK, C, true>::kBytes, 0, 0);
+    a.ws_qk = static_cast<unsigned char*>(a.ws) + wl.qk;  // right after the blocks
   }
   const hipError_t err = launch_prep<OpT, DK, C>(a, all, stream);
   if (err != hipSuccess) return err;

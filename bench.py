@@ -63,7 +63,7 @@ def up(a):
 
 
 def cpu_threads() -> int:
-    # The GPU machine gives one GPU a 16-core share, whatever os.cpu_count() says.
+    # At most 16 host threads: the host's share per GPU, whatever os.cpu_count() reports.
     return max(1, min(16, os.cpu_count() or 1))
 
 

@@ -8,8 +8,8 @@ import torch
 import gated_delta_rule_40_amd as gdr
 import oracle
 from gated_delta_rule_40_amd import synth
-from tests.gpu_util import (DEV, TOL, announce, carry_segments, oracle_threads, rel, require_gpu,
-                            run_prefill, to_dev, to_host)
+from tests.gpu_util import (DEV, TOL, announce, carry_segments, io_dtype, oracle_threads, rel,
+                            require_gpu, run_prefill, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -475,3 +475,40 @@ def test_prefill_t0_copies_state():
                             H_qk=1, H_v=2, dk=16, dv=16, chunk=16, gate=synth.GATE_CHANNEL)
     torch.cuda.synchronize()
     assert torch.equal(s_in, s_out)
+
+
+# Every byte a chunked prefill writes lies inside the workspace the size query
+# asks for: the workspace is a view at the start of a larger buffer whose tail
+# (64 KiB) holds a byte pattern that must come back unchanged.  Both gate
+# layouts (the channel gate's blocks; the scalar gate's smaller blocks plus
+# the per-qk-head rows), the plain and the segmented carry, both io dtypes.
+@pytest.mark.parametrize("B,T,H_qk,H_v,dk,dv,chunk,io,gate", [
+    (2, 333, 2, 4, 64, 64, 32, "bf16", synth.GATE_CHANNEL),
+    (2, 333, 2, 4, 64, 64, 32, "bf16", synth.GATE_SCALAR),
+    (1, 2500, 1, 2, 64, 64, 32, "bf16", synth.GATE_CHANNEL),
+    (1, 2500, 1, 2, 64, 64, 32, "f32", synth.GATE_SCALAR_FUSED),
+    (4, 130, 16, 32, 128, 128, 64, "bf16", synth.GATE_SCALAR),
+])
+def test_prefill_writes_stay_in_workspace(B, T, H_qk, H_v, dk, dv, chunk, io, gate):
+    require_gpu()
+    case = synth.prefill_case("canary", 480 + T % 89 + gate, B, T, H_qk, H_v, dk, dv, chunk, io,
+                              gate, 0.01, 0.3, 0.3)
+    n = gdr.gdr_prefill_workspace_size(B, T, H_qk, H_v, dk, dv, chunk, io_dtype(io), gate)
+    pad = 64 << 10
+    announce(f"prefill workspace bounds: B={B} T={T} H {H_qk}->{H_v} dk={dk} dv={dv} chunk={chunk} "
+             f"io={io} gate={gate} workspace {n} B, carry segments "
+             f"{carry_segments(B, T, H_v, dk, dv, chunk)}")
+    buf = torch.empty(n + pad, dtype=torch.uint8, device=DEV)
+    pattern = (torch.arange(pad, device=DEV, dtype=torch.int32) * 37 + 11).remainder(251).to(torch.uint8)
+    buf[n:] = pattern
+    t = case.tensors
+    S = torch.empty((B, H_v, dk, dv), dtype=torch.float32, device=DEV)
+    o = torch.empty((B, T, H_v, dv), dtype=io_dtype(io), device=DEV)
+    gdr.gdr_prefill_chunked(to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"]), to_dev(t["gate_in"]),
+                            to_dev(t["beta_logit"]), to_dev(t["S0"]), S, o, buf[:n], H_qk=H_qk,
+                            H_v=H_v, dk=dk, dv=dv, chunk=chunk, gate=gate,
+                            A_log=to_dev(t["A_log"]), dt_bias=to_dev(t["dt_bias"]))
+    torch.cuda.synchronize()
+    assert torch.equal(buf[n:], pattern), "a prefill wrote past its workspace"
+    o_ref, S_ref = _oracle(case)
+    assert rel(to_host(o), o_ref) < TOL[io] and rel(to_host(S), S_ref) < TOL[io]

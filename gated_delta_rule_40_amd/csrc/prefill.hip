@@ -202,6 +202,16 @@ struct QKRegion {
   static constexpr size_t kBytes = 2 * static_cast<size_t>(C) * DK * sizeof(OpT);
 };
 
+// The workspace is chunk-major: block (b, chunk n, value head h) is number
+// (b * NC + n) * H_v + h, and the QKRegion of (b, n, qk head hq) number
+// (b * NC + n) * H_qk + hq.  The blocks that one chunk step of the carry reads
+// (chunk n of every head) and that neighbouring prep units write then lie
+// side by side.
+template <typename Blk>
+__device__ __forceinline__ size_t block_offset(int b, int n, int h, int NC, int H_v) {
+  return ((static_cast<size_t>(b) * NC + n) * H_v + h) * Blk::kBytes;
+}
+
 // ---------------------------------------------------------------------------
 // chunk_prep
 //
@@ -879,26 +889,27 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
   const int wave = tid >> 6;
   const int NC = (a.T + C - 1) / C;
   const int NCr = cr.n1 - cr.n0;
-  // Work order: the rep = H_v / H_qk value heads that share a qk head, for one
-  // chunk, are consecutive units, and consecutive units run on one XCD
-  // (workgroups w, w + 8, ... share an XCD), so all but the first read that
-  // chunk's q and k rows from the XCD's L2.
+  // Work order: every value head of one (b, chunk) is a run of consecutive
+  // units, the rep = H_v / H_qk heads that share a qk head next to each other,
+  // and consecutive units run on one XCD (workgroups w, w + 8, ... share an
+  // XCD).  One cache line of beta (and of a per-head gate) holds every head's
+  // value for a token, and the rep heads read the same q and k rows, so those
+  // lines come from HBM about once and from the XCD's L2 after that.
   int unit = wg;
   if (G % 8 == 0) unit = (wg % 8) * (G / 8) + wg / 8;
   const int rep = a.H_v / a.H_qk;
   const int r_in = unit % rep;
-  const int n = cr.n0 + (unit / rep) % NCr;
-  const int bq = unit / (rep * NCr);  // b * H_qk + hq
-  const int hq = bq % a.H_qk;
-  const int b = bq / a.H_qk;
+  const int hq = (unit / rep) % a.H_qk;
+  const int bn = unit / a.H_v;  // b * NCr + (n - n0)
+  const int n = cr.n0 + bn % NCr;
+  const int b = bn / NCr;
   const int h = hq * rep + r_in;
-  const int bh = b * a.H_v + h;
   const int t0 = n * C;
   const int L = min(C, a.T - t0);
   const OpT* qg = static_cast<const OpT*>(a.q);
   const OpT* kg = static_cast<const OpT*>(a.k);
   unsigned char* blk_bytes =
-      static_cast<unsigned char*>(a.ws) + (static_cast<size_t>(bh) * NC + n) * Blk::kBytes;
+      static_cast<unsigned char*>(a.ws) + block_offset<Blk>(b, n, h, NC, a.H_v);
   const size_t qk_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_qk + hq;  // row t0
   const size_t g_row0 = (static_cast<size_t>(b) * a.T + t0) * a.H_v + h;
 
@@ -1043,7 +1054,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
   //         is used only where its e^-Gamma stays small ----
   if constexpr (!kChannel) {
     OpT* qk_out = r_in == 0 ? static_cast<OpT*>(a.ws_qk) +
-                                  (static_cast<size_t>(bq) * NC + n) * (2 * C * DK)
+                                  ((static_cast<size_t>(b) * NC + n) * a.H_qk + hq) * (2 * C * DK)
                             : nullptr;
     prep_causal_scalar<OpT, DK, C>(kq, qq, gq, gam0[0], total[0], L, rlo, active, c4, out, qk_out,
                                    sm, tid, lane, wave);
@@ -1236,7 +1247,7 @@ template <typename OpT, int DK, int C>
 __device__ __forceinline__ const OpT* qk_region(const PrefillArgs& a, int b, int hq, int nn) {
   const int NC = (a.T + C - 1) / C;
   return static_cast<const OpT*>(a.ws_qk) +
-         ((static_cast<size_t>(b) * a.H_qk + hq) * NC + nn) * (2 * C * DK);
+         ((static_cast<size_t>(b) * NC + nn) * a.H_qk + hq) * (2 * C * DK);
 }
 
 // kScalarGate: the row factors e^Gamma of output tile row-block R in accumulator
@@ -1281,7 +1292,7 @@ __device__ __forceinline__ void carry_load(CarryFrags<OpT, DK, DVS, C, kScalarGa
   using Blk = typename Sh::Blk;
   using FK = typename Sh::FK;
   using FC = typename Sh::FC;
-  const unsigned char* blk_bytes = ws_head + static_cast<size_t>(nn) * Blk::kBytes;
+  const unsigned char* blk_bytes = ws_head + static_cast<size_t>(nn) * a.H_v * Blk::kBytes;
   const OpT* blk = reinterpret_cast<const OpT*>(blk_bytes);
   const OpT* vg = static_cast<const OpT*>(a.v);
   const int t0 = nn * C;
@@ -1451,7 +1462,7 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
 
   const size_t st_off = static_cast<size_t>(bh) * DK * a.dv;
   const unsigned char* ws_head =
-      static_cast<const unsigned char*>(a.ws) + static_cast<size_t>(bh) * NC * Blk::kBytes;
+      static_cast<const unsigned char*>(a.ws) + block_offset<Blk>(b, 0, h, NC, a.H_v);
   OpT* og = static_cast<OpT*>(a.o);
 
   // ---- state tiles owned by this wave, in accumulator layout ----
@@ -1490,7 +1501,8 @@ __device__ __forceinline__ void carry_body(const PrefillArgs& a, ChunkRange cr,
     const int t0 = nn * C;
     const int L = kFull ? C : min(C, a.T - t0);
     const int nx = min(nn + 1, cr.n1 - 1);
-    const OpT* nblk = reinterpret_cast<const OpT*>(ws_head + static_cast<size_t>(nx) * Blk::kBytes);
+    const OpT* nblk =
+        reinterpret_cast<const OpT*>(ws_head + static_cast<size_t>(nx) * a.H_v * Blk::kBytes);
     const OpT* nqk = kScalarGate ? qk_region<OpT, DK, C>(a, b, hq, nx) : nullptr;
     // S^T in the operand type, for Kt S and Qt S.
 #pragma unroll

@@ -238,7 +238,7 @@ __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <typename OpT, int DK, int C>
+template <typename OpT, int DK, int C, bool kScalarGate = false>
 struct PrepSmem {
   static constexpr int LDK = DK + pad_of<OpT>();  // rows of Kt, Kh, Ke, Qt
   static constexpr int LDT = C + 4;               // fp32 A (row-major), T (column-major)
@@ -260,15 +260,27 @@ struct PrepSmem {
   static constexpr size_t kX = 4 * 16 * LDX * sizeof(float);
   static constexpr size_t kN = static_cast<size_t>(C) * LDN * sizeof(float);
   static constexpr size_t kG = static_cast<size_t>(PARTS) * DK * sizeof(float);
-  // Three regions, each reused as the chunk moves on (a barrier between uses):
+  // Channel gates: three regions, each reused as the chunk moves on (a
+  // barrier between uses):
   //   R0: row-norm partials -> operand rows (Kt, Qt, K, ...) -> solve scratch
   //   R1: operand rows (Kh, Ke, Q, ...) -> T, column-major
   //   R2: per-part channel sums of the prefix -> A
   // (R0 + R1 also stage the exact routine's fp32 passes.)
+  // Scalar gates need only the K and Q rows at once (P goes straight to the
+  // block and A waits in registers until the Q rows are dead), so two regions
+  // and the solve scratch do: 40,960 bytes in all at dk = 128, C = 64, bf16,
+  // which lets four workgroups share a CU instead of three.
+  //   R0: row-norm partials -> K rows -> Ke rows -> T, column-major
+  //   R1: Q rows -> A
+  //   X:  per-part sums of the prefix -> solve scratch
   static constexpr size_t oR0 = 0;
-  static constexpr size_t oR1 = al16(mx(mx(kOpRows, kN), kX));
+  static constexpr size_t oR1 = al16(mx(mx(kOpRows, kN), kScalarGate ? kTm : kX));
   static constexpr size_t oR2 = oR1 + al16(mx(kOpRows, kTm));
-  static constexpr size_t kBytes = oR2 + al16(mx(kTm, kG));
+  static constexpr size_t oX = kScalarGate ? oR2 : oR0;  // solve scratch
+  static constexpr size_t oT = kScalarGate ? oR0 : oR1;  // T, column-major
+  static constexpr size_t oA = kScalarGate ? oR1 : oR2;  // A, row-major
+  static constexpr size_t oG = oR2;                      // prefix partials
+  static constexpr size_t kBytes = oR2 + al16(kScalarGate ? mx(kX, kG) : mx(kTm, kG));
   static constexpr size_t oBeta = kBytes;  // beta of the chunk's rows
   static constexpr size_t oGam = oBeta + al16(static_cast<size_t>(C) * sizeof(float));  // scalar gate: Gamma per row
   static constexpr size_t oNrm = oGam + al16(static_cast<size_t>(C) * sizeof(float));   // 1/|k|, 1/|q| per row
@@ -415,12 +427,12 @@ __device__ __forceinline__ void prep_causal_scalar(
     const typename PrepSmem<OpT, DK, C>::RowsF& kq, const typename PrepSmem<OpT, DK, C>::RowsF& qq,
     const typename PrepSmem<OpT, DK, C>::RowsF& gq, float gam0, float total, int L, int rlo,
     bool active, int c4, OpT* out, OpT* qk_out, unsigned char* sm, int tid, int lane, int wave) {
-  using Sm = PrepSmem<OpT, DK, C>;
+  using Sm = PrepSmem<OpT, DK, C, true>;
   using Blk = ChunkBlock<OpT, DK, C, true>;
   constexpr int LDK = Sm::LDK, LDT = Sm::LDT, NB = Sm::NB, RPP = Sm::RPP;
-  OpT* Kr_s = reinterpret_cast<OpT*>(sm + Sm::oR0);  // K rows as given
+  OpT* Kr_s = reinterpret_cast<OpT*>(sm + Sm::oR0);  // K rows as given, then the Ke rows
   OpT* Qr_s = reinterpret_cast<OpT*>(sm + Sm::oR1);  // Q rows as given
-  float* A_s = reinterpret_cast<float*>(sm + Sm::oR2);
+  float* A_s = reinterpret_cast<float*>(sm + Sm::oA);  // where the Q rows were
   float* gam_s = reinterpret_cast<float*>(sm + Sm::oGam);
   const float* beta_s = reinterpret_cast<const float*>(sm + Sm::oBeta);
 
@@ -456,29 +468,36 @@ __device__ __forceinline__ void prep_causal_scalar(
 
   // Lower tiles: A and P of a tile by one wave, computed transposed (each
   // lane holds four consecutive columns of one row) with one shared decay
-  // factor per entry; tiles above the diagonal of P are zeros.
+  // factor per entry; tiles above the diagonal of P are zeros.  P goes
+  // straight to the block; a wave's A tiles stay in registers until the Q
+  // rows are dead.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int NW = kThreads / 64;
   constexpr int NL = NB * (NB + 1) / 2;
-  for (int job = wv; job < NL; job += kThreads / 64) {
-    int R, S;
-    lower_tile(job, R, S);
-    f32x4 ga = {0.f, 0.f, 0.f, 0.f}, gp = {0.f, 0.f, 0.f, 0.f};
-    ga = mma_xzt<OpT, DK>(Kr_s, LDK, 16 * S, Kr_s, LDK, 16 * R, ga, lane);
-    gp = mma_xzt<OpT, DK>(Kr_s, LDK, 16 * S, Qr_s, LDK, 16 * R, gp, lane);
-    const int row = 16 * R + (lane & 15);
-    const int col = 16 * S + 4 * (lane >> 4);
-    const float gr = gam_s[row], br = beta_s[row];
-    float av[4];
-    OpT pv[4];
+  constexpr int NJ = (NL + NW - 1) / NW;  // lower tiles per wave, at most
+  float av[NJ][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = col + e;
-      const float f = row >= c ? __builtin_amdgcn_exp2f((gr - gam_s[c]) * kLog2e) : 0.0f;
-      av[e] = row > c ? br * f * ga[e] : 0.0f;
-      pv[e] = from_f32<OpT>(f * gp[e]);
+  for (int j = 0; j < NJ; ++j) {
+    const int job = wv + j * NW;
+    if (job < NL) {
+      int R, S;
+      lower_tile(job, R, S);
+      f32x4 ga = {0.f, 0.f, 0.f, 0.f}, gp = {0.f, 0.f, 0.f, 0.f};
+      ga = mma_xzt<OpT, DK>(Kr_s, LDK, 16 * S, Kr_s, LDK, 16 * R, ga, lane);
+      gp = mma_xzt<OpT, DK>(Kr_s, LDK, 16 * S, Qr_s, LDK, 16 * R, gp, lane);
+      const int row = 16 * R + (lane & 15);
+      const int col = 16 * S + 4 * (lane >> 4);
+      const float gr = gam_s[row], br = beta_s[row];
+      OpT pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = col + e;
+        const float f = row >= c ? __builtin_amdgcn_exp2f((gr - gam_s[c]) * kLog2e) : 0.0f;
+        av[j][e] = row > c ? br * f * ga[e] : 0.0f;
+        pv[e] = from_f32<OpT>(f * gp[e]);
+      }
+      frag_store<OpT, C, 4>(out + Blk::kP, row, col, pv);
     }
-    *reinterpret_cast<float4*>(A_s + row * LDT + col) = make_float4(av[0], av[1], av[2], av[3]);
-    frag_store<OpT, C, 4>(out + Blk::kP, row, col, pv);
   }
   for (int job = wv; job < NB * NB; job += kThreads / 64) {
     const int R = job / NB, S = job % NB;
@@ -488,10 +507,22 @@ __device__ __forceinline__ void prep_causal_scalar(
       frag_store<OpT, C, 4>(out + Blk::kP, 16 * R + (lane & 15), 16 * S + 4 * (lane >> 4), z);
     }
   }
-  __syncthreads();  // K and Q rows are dead: Ke^T through R1, transposed
-  if (active) rows_to_lds<OpT, RPP>(Qr_s, LDK, rlo, c4, ker);
+  __syncthreads();  // K and Q rows are dead: A where the Q rows were, Ke^T through R0
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int job = wv + j * NW;
+    if (job < NL) {
+      int R, S;
+      lower_tile(job, R, S);
+      const int row = 16 * R + (lane & 15);
+      const int col = 16 * S + 4 * (lane >> 4);
+      *reinterpret_cast<float4*>(A_s + row * LDT + col) =
+          make_float4(av[j][0], av[j][1], av[j][2], av[j][3]);
+    }
+  }
+  if (active) rows_to_lds<OpT, RPP>(Kr_s, LDK, rlo, c4, ker);
   __syncthreads();
-  lds_to_frag_t<OpT, C, DK>(out + Blk::kKeT, Qr_s, LDK, tid);
+  lds_to_frag_t<OpT, C, DK>(out + Blk::kKeT, Kr_s, LDK, tid);
   __syncthreads();
 }
 
@@ -872,17 +903,17 @@ __device__ __forceinline__ void prep_causal_exact(const PrefillArgs& a, size_t q
 template <typename OpT, int DK, int C, bool kChannel>
 __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, int wg, int G,
                                           unsigned char* sm) {
-  using Sm = PrepSmem<OpT, DK, C>;
+  using Sm = PrepSmem<OpT, DK, C, !kChannel>;
   using Blk = ChunkBlock<OpT, DK, C, !kChannel>;
   constexpr int LDT = Sm::LDT, LDX = Sm::LDX, NB = Sm::NB;
   constexpr int PARTS = Sm::PARTS, RPP = Sm::RPP;
 
   float* beta_s = reinterpret_cast<float*>(sm + Sm::oBeta);
 
-  float* X_s = reinterpret_cast<float*>(sm + Sm::oR0);   // solve scratch
-  float* TT_s = reinterpret_cast<float*>(sm + Sm::oR1);  // T column-major: TT[s][r] = T[r][s]
-  float* gpart = reinterpret_cast<float*>(sm + Sm::oR2); // [PARTS][DK]
-  float* A_s = reinterpret_cast<float*>(sm + Sm::oR2);   // A row-major
+  float* X_s = reinterpret_cast<float*>(sm + Sm::oX);    // solve scratch
+  float* TT_s = reinterpret_cast<float*>(sm + Sm::oT);   // T column-major: TT[s][r] = T[r][s]
+  float* gpart = reinterpret_cast<float*>(sm + Sm::oG);  // [PARTS][DK]
+  float* A_s = reinterpret_cast<float*>(sm + Sm::oA);    // A row-major
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1155,7 +1186,7 @@ __device__ __forceinline__ void prep_body(const PrefillArgs& a, ChunkRange cr, i
 
 template <typename OpT, int DK, int C, bool kChannel>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, ChunkRange cr) {
-  __shared__ __attribute__((aligned(16))) unsigned char sm[PrepSmem<OpT, DK, C>::kAll];
+  __shared__ __attribute__((aligned(16))) unsigned char sm[PrepSmem<OpT, DK, C, !kChannel>::kAll];
   prep_body<OpT, DK, C, kChannel>(a, cr, blockIdx.x, gridDim.x, sm);
 }
 

@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -67,10 +68,25 @@ def cpu_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with its comments removed and every run of whitespace made
+    one space: what the compiler sees, so a change to comments alone keeps the
+    digest."""
+    def keep(m):
+        t = m.group(0)
+        return " " if t.startswith("/") else t
+    return " ".join(_CODE_TOKENS.sub(keep, src).split())
+
+
 def source_digest(*names) -> str:
+    """Digest of the code (comments and whitespace aside) of kernel sources."""
     h = hashlib.sha256()
     for n in names:
-        h.update((ROOT / "gated_delta_rule_40_amd" / "csrc" / n).read_bytes())
+        src = (ROOT / "gated_delta_rule_40_amd" / "csrc" / n).read_text()
+        h.update(code_text(src).encode())
     return h.hexdigest()[:16]
 
 

@@ -231,8 +231,9 @@ __device__ __forceinline__ size_t block_offset(int b, int n, int h, int NC, int 
 //      substitution in registers (one lane per column), then the off-diagonal
 //      blocks level by level, T_ij = -T_ii sum_k A_ik T_kj, with fp32 MFMA;
 //   6. Tb = T diag(beta) leaves for the block in coalesced lane slices.
-// LDS holds three regions that are reused phase by phase (PrepSmem), small
-// enough for three workgroups per CU at dk = 128, C = 64, bf16.
+// LDS holds regions that are reused phase by phase (PrepSmem): three with a
+// channel gate (three workgroups per CU at dk = 128, C = 64, bf16), two and
+// the solve scratch with a scalar gate (four per CU).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -2041,10 +2042,10 @@ size_t seg_bytes(SegPlan sp, long units, int dk, int dv) {
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace layout: the chunk blocks ((b, h)-major, then chunk); at the next
-// 256-byte boundary, for scalar gates, the QKRegions ((b, qk head)-major, then
-// chunk); at the next 256-byte boundary, the segmented carry's buffers (if it
-// runs).
+// Workspace layout: the chunk blocks (chunk-major: (b, chunk, h), see
+// block_offset); at the next 256-byte boundary, for scalar gates, the
+// QKRegions ((b, chunk, qk head)); at the next 256-byte boundary, the
+// segmented carry's buffers (if it runs).
 struct WsLayout {
   size_t qk, seg, total;
 };

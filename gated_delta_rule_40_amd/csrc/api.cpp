@@ -51,6 +51,9 @@ int check_sizes(const gdr_dims* d, gdr_dtype io, gdr_gate gate, bool prefill) {
   if (prefill) {
     const long long chunks = (static_cast<long long>(d->T) + d->chunk - 1) / d->chunk;
     if (units * chunks > INT32_MAX) return GDR_E_SHAPE;
+    // The carry reaches a chunk's v and o rows through 32-bit element offsets
+    // from the chunk's first row (token stride H_v * dv).
+    if (static_cast<long long>(d->chunk) * d->H_v * d->dv > UINT32_MAX) return GDR_E_SHAPE;
   }
   return GDR_OK;
 }

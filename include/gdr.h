@@ -39,6 +39,9 @@
  *     buffer is touched.  GDR_E_HIP reports a failed launch.
  *   - Supported sizes: dk, dv in {16, 32, 64, 128}; H_v a multiple of H_qk;
  *     chunk in {16, 32, 64}.  B = 0 (and T = 0 for prefill) is a valid no-op.
+ *     GDR_E_SHAPE also reports sizes past the 32-bit limits of the launch:
+ *     B * H_v * dv and, for prefill, B * H_v * ceil(T / chunk) at most
+ *     2^31 - 1, and chunk * H_v * dv at most 2^32 - 1.
  */
 #ifndef GDR_H_
 #define GDR_H_

@@ -123,6 +123,8 @@ def test_decode_validation(case, expect):
     (dict(gate=2, Al=A + 0x7000010, dt=A + 0x8000000), "ALIAS"),  # A_log under o
     (dict(gate=2, Al=A + 0x8000000, dt=A + 0x10000000), "ALIAS"),  # dt_bias in the workspace
     (dict(gate=2, Al=A + 0x6000000, dt=A + 0x8000000), "ALIAS"),  # A_log under state_out
+    # 64 tokens x 2^19 heads x 128 columns: the carry's 32-bit row offsets would wrap
+    (dict(dims=_dims(B=1, H_qk=1, H_v=1 << 19, dv=128, chunk=64)), "SHAPE"),
     (dict(dims=_dims(B=0)), "OK"),
     (dict(dims=_dims(T=0), s_in=A + 0x6000000), "OK"),   # T=0, in place: nothing to copy
     (dict(dims=_dims(T=0), s_out=A + 0x5000100), "ALIAS"),  # T=0, shifted copy
